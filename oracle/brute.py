@@ -1,0 +1,41 @@
+"""Scalar brute-force causal GQA: pure-Python loops, ``math.fsum`` and ``math.exp``.
+
+TEST INFRASTRUCTURE ONLY (like ``oracle.oracle``): a second, independent
+writing of the same definition, used on tiny shapes to cross-check the NumPy
+oracle. It touches no NumPy arithmetic: every score, weight and output is a
+Python float built from exactly rounded sums.
+
+For query head ``h`` the KV head is ``h // (n_heads // n_kv_heads)``; query
+row ``i`` at absolute position ``position_offset + i`` sees keys
+``j <= position_offset + i`` (kopitiam-runtime 0.2.4 ``src/attention.rs``,
+module doc and ``causal_mask``). Weights are ``exp(s_j - max s) / sum``.
+"""
+from __future__ import annotations
+
+import math
+
+__all__ = ["gqa_attention"]
+
+
+def gqa_attention(q, k, v, n_heads, n_kv_heads, position_offset, scale):
+    """``q[i][h][c]``, ``k[j][g][c]``, ``v[j][g][c]`` nested sequences -> ``out[i][h][c]``."""
+    assert n_kv_heads > 0 and n_heads % n_kv_heads == 0
+    group = n_heads // n_kv_heads
+    seq_q, seq_kv = len(q), len(k)
+    dv = len(v[0][0]) if seq_kv else 0
+    out = []
+    for i in range(seq_q):
+        row = []
+        last = position_offset + i
+        visible = [j for j in range(seq_kv) if j <= last]
+        for h in range(n_heads):
+            g = h // group
+            s = [scale * math.fsum(float(q[i][h][c]) * float(k[j][g][c]) for c in range(len(q[i][h])))
+                 for j in visible]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = math.fsum(w)
+            row.append([math.fsum(w[n] * float(v[j][g][c]) for n, j in enumerate(visible)) / z
+                        for c in range(dv)])
+        out.append(row)
+    return out

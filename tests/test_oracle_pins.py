@@ -1,0 +1,332 @@
+"""Pins for the float64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every check is a value the
+pages print (tests/golden), a closed form, a library routine that computes
+the same special case (torch's scaled_dot_product_attention on the CPU in
+float64), an invariant, or the independent brute-force form.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "kopitiam_attention_unit_values.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _vals(lst):
+    return np.array([-np.inf if x == "-inf" else x for x in lst], dtype=np.float64)
+
+
+# ---------------------------------------------------------------- page values
+
+def test_golden_repeat_kv_heads_shares():
+    g = _golden()["repeat_kv_heads_shares"]
+    x = np.array(g["input"]).reshape(g["input_shape"])
+    y = O.repeat_kv_heads(x, g["group_size"])
+    assert list(y.shape) == g["expected_shape"]
+    d = y.reshape(-1)
+    assert d.tolist() == g["expected"]
+    assert d[0] == d[1] and d[2] == d[3] and d[0] != d[2]
+
+
+def test_golden_repeat_kv_heads_identity():
+    g = _golden()["repeat_kv_heads_identity"]
+    x = np.array(g["input"]).reshape(g["input_shape"])
+    assert O.repeat_kv_heads(x, 1).reshape(-1).tolist() == g["expected"]
+
+
+@pytest.mark.parametrize("key", ["mask_prefill_3x3", "mask_decode_offset"])
+def test_golden_masks(key):
+    g = _golden()[key]
+    m = O.causal_mask(g["seq_q"], g["seq_kv"], g["position_offset"]).reshape(-1)
+    exp = _vals(g["expected"])
+    assert np.array_equal(m, exp)
+    assert np.all(np.isneginf(m) == np.isneginf(exp))
+
+
+def test_golden_mask_is_exact_neg_inf():
+    g = _golden()["mask_exact_neg_inf"]
+    m = O.causal_mask(g["seq_q"], g["seq_kv"], g["position_offset"]).reshape(-1)
+    assert m[g["index"]] == -np.inf
+
+
+def test_golden_masked_softmax_exact_zeros():
+    g = _golden()["masked_softmax_zero_weight"]
+    s = np.array(g["scores"]).reshape(1, 1, -1)
+    p = O.masked_softmax(s, O.causal_mask(g["seq_q"], g["seq_kv"], g["position_offset"])).reshape(-1)
+    assert abs(p[0] - 1.0) < g["atol_first"]
+    assert p[1] == 0.0 and p[2] == 0.0
+
+
+def test_golden_zero_kv_gives_zero_output():
+    g = _golden()["zero_kv_zero_output"]
+    x = (np.arange(g["seq"] * g["hidden"]) * 0.1).reshape(g["seq"], g["n_heads"], g["head_dim"])
+    z = np.zeros((g["seq"], g["n_kv_heads"], g["head_dim"]))
+    out = O.gqa_attention(x, z, z, g["n_heads"], g["n_kv_heads"], 0, 1 / math.sqrt(g["head_dim"]))
+    assert out.shape == (g["seq"], g["n_heads"], g["head_dim"])
+    assert np.all(out == 0.0)
+
+
+# ------------------------------------------------------------ library routine
+
+def _sdpa(q, k, v, n_heads, n_kv_heads, off, scale):
+    """torch SDPA (float64, CPU) with enable_gqa and a boolean lower-triangular mask."""
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None].double()
+    tk = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None].double()
+    tv = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None].double()
+    allowed = torch.ones(q.shape[0], k.shape[0], dtype=torch.bool).tril(diagonal=off)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=allowed, scale=scale, enable_gqa=(n_heads != n_kv_heads))
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("H,Hkv,D,Dv,sq,off,seed", [
+    (4, 4, 8, 8, 9, 0, 0),       # plain MHA (group size 1)
+    (6, 2, 16, 16, 17, 0, 1),    # GQA prefill
+    (8, 2, 16, 16, 5, 11, 2),    # chunk after cached tokens
+    (4, 1, 32, 24, 1, 40, 3),    # MQA decode, value width differs
+    (28, 4, 128, 128, 33, 7, 4), # the large prefill's head layout
+])
+def test_oracle_matches_torch_sdpa(H, Hkv, D, Dv, sq, off, seed):
+    rng = np.random.default_rng(seed)
+    skv = off + sq
+    q = rng.standard_normal((sq, H, D))
+    k = rng.standard_normal((skv, Hkv, D))
+    v = rng.standard_normal((skv, Hkv, Dv))
+    scale = 0.3 + 0.1 * seed
+    ref = _sdpa(q, k, v, H, Hkv, off, scale)
+    got = O.gqa_attention(q, k, v, H, Hkv, off, scale)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_sdpa_causal_flag_agrees_at_offset_zero():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((12, 4, 8))
+    k = rng.standard_normal((12, 2, 8))
+    v = rng.standard_normal((12, 2, 8))
+    tq = torch.from_numpy(q.transpose(1, 0, 2).copy())[None]
+    tk = torch.from_numpy(k.transpose(1, 0, 2).copy())[None]
+    tv = torch.from_numpy(v.transpose(1, 0, 2).copy())[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.5,
+                                                           enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+    np.testing.assert_allclose(O.gqa_attention(q, k, v, 4, 2, 0, 0.5), ref, rtol=0, atol=1e-12)
+
+
+# -------------------------------------------------------------- closed forms
+
+def test_two_key_closed_form():
+    # scores (0, ln 3) give weights (1/4, 3/4); the query at position 1 sees both keys.
+    q = np.array([[[1.0]]])
+    k = np.array([[[0.0]], [[math.log(3.0)]]])
+    v = np.array([[[4.0, -8.0]], [[8.0, 4.0]]])
+    got = O.gqa_attention(q, k, v, 1, 1, 1, 1.0)[0, 0]
+    np.testing.assert_allclose(got, [7.0, 1.0], rtol=0, atol=1e-14)
+    # The same query at position 0 may see key 0 only: output is v[0].
+    got0 = O.gqa_attention(q, k, v, 1, 1, 0, 1.0)[0, 0]
+    assert np.array_equal(got0, v[0, 0])
+
+
+def test_zero_keys_give_mean_of_visible_values():
+    rng = np.random.default_rng(11)
+    sq, off, H, Hkv, D = 6, 3, 4, 2, 5
+    q = rng.standard_normal((sq, H, D))
+    k = np.zeros((off + sq, Hkv, D))
+    v = rng.standard_normal((off + sq, Hkv, D))
+    out = O.gqa_attention(q, k, v, H, Hkv, off, 0.7)
+    for i in range(sq):
+        for h in range(H):
+            np.testing.assert_allclose(out[i, h], v[:off + i + 1, h // (H // Hkv)].mean(axis=0),
+                                       rtol=0, atol=1e-14)
+
+
+def test_constant_values_give_that_constant():
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((7, 6, 4))
+    k = rng.standard_normal((7, 3, 4))
+    v = np.full((7, 3, 4), -2.5)
+    assert np.allclose(O.gqa_attention(q, k, v, 6, 3, 0, 1.3), -2.5, rtol=0, atol=1e-14)
+    assert np.all(O.gqa_attention(q, k, np.zeros_like(v), 6, 3, 0, 1.3) == 0.0)
+
+
+def test_first_row_is_first_value_of_its_kv_head():
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((5, 8, 3))
+    k = rng.standard_normal((5, 2, 3))
+    v = rng.standard_normal((5, 2, 3))
+    out = O.gqa_attention(q, k, v, 8, 2, 0, 2.0)
+    for h in range(8):
+        assert np.array_equal(out[0, h], v[0, h // 4])
+
+
+def test_hard_attention_limit_picks_the_best_key():
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((1, 2, 6))
+    k = rng.standard_normal((9, 1, 6))
+    v = rng.standard_normal((9, 1, 6))
+    out = O.gqa_attention(q, k, v, 2, 1, 8, 1e4)
+    for h in range(2):
+        j = int(np.argmax(k[:, 0] @ q[0, h]))
+        np.testing.assert_allclose(out[0, h], v[j, 0], rtol=0, atol=1e-9)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_group_members_share_kv_and_only_their_group_moves():
+    rng = np.random.default_rng(15)
+    H, Hkv, G, D = 6, 3, 2, 4
+    qrow = rng.standard_normal((4, 1, D))
+    q = np.repeat(qrow, H, axis=1)          # identical query in every head
+    k = rng.standard_normal((4, Hkv, D))
+    v = rng.standard_normal((4, Hkv, D))
+    base = O.gqa_attention(q, k, v, H, Hkv, 0, 0.5)
+    for g in range(Hkv):
+        for h in range(g * G, (g + 1) * G):
+            assert np.array_equal(base[:, h], base[:, g * G])
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 1] += 1.0
+    v2[:, 1] -= 0.5
+    moved = O.gqa_attention(q, k2, v2, H, Hkv, 0, 0.5)
+    for h in range(H):
+        same = np.array_equal(moved[:, h], base[:, h])
+        assert same == (h // G != 1), h
+
+
+def test_outputs_are_convex_combinations_of_visible_values():
+    rng = np.random.default_rng(16)
+    sq, off, H, Hkv, D = 5, 4, 4, 4, 6
+    q = rng.standard_normal((sq, H, D)) * 3
+    k = rng.standard_normal((off + sq, Hkv, D))
+    v = rng.standard_normal((off + sq, Hkv, D))
+    out = O.gqa_attention(q, k, v, H, Hkv, off, 1.0)
+    for i in range(sq):
+        vis = v[:off + i + 1]
+        assert np.all(out[i] <= vis.max(axis=0) + 1e-12)
+        assert np.all(out[i] >= vis.min(axis=0) - 1e-12)
+
+
+def test_decode_step_equals_prefill_row():
+    rng = np.random.default_rng(17)
+    T, H, Hkv, D = 20, 4, 2, 8
+    q = rng.standard_normal((1, T, H, D))
+    k = rng.standard_normal((1, T, Hkv, D))
+    v = rng.standard_normal((1, T, Hkv, D))
+    full = O.prefill(q, k, v, H, Hkv, T, 0, 0.4)
+    for L in range(1, T + 1):
+        dec = O.decode_contig(q[:, L - 1], k, v, [L], H, Hkv, 0.4)
+        np.testing.assert_allclose(dec[0], full[0, L - 1], rtol=0, atol=1e-13)
+
+
+def test_paged_equals_contiguous_and_is_block_permutation_invariant():
+    from paged_kv_attention_causal_amd import inputs
+    case = inputs.paged_decode_case(3, dtype="f32", batch=5, len_lo=1, len_hi=70, n_heads=4,
+                                    n_kv_heads=2, head_dim=8, block_size=16)
+    kc, vc = case.contig()
+    a = O.decode_paged(case.q, case.k_pool, case.v_pool, case.block_table, 16, case.seq_lens, 4, 2,
+                       case.scale)
+    b = O.decode_contig(case.q, kc, vc, case.seq_lens, 4, 2, case.scale)
+    assert np.array_equal(a, b)
+    # Permute the pool's blocks and rename the table entries to match.
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(case.k_pool.shape[0])
+    inv = np.argsort(perm)
+    kp2, vp2 = case.k_pool[perm], case.v_pool[perm]
+    bt2 = np.where(case.block_table >= 0, inv[np.maximum(case.block_table, 0)], -1)
+    c = O.decode_paged(case.q, kp2, vp2, bt2, 16, case.seq_lens, 4, 2, case.scale)
+    assert np.array_equal(a, c)
+
+
+def test_paged_prefill_equals_contiguous_prefill():
+    from paged_kv_attention_causal_amd import inputs
+    case = inputs.chunked_paged_prefill_case(5, dtype="f32", batch=2, cached=21, seq_q=11, n_heads=4,
+                                             n_kv_heads=2, head_dim=8, block_size=4, scale=0.3)
+    paged = O.prefill(case.q, case.k, case.v, 4, 2, case.seq_kv, case.position_offset, case.scale,
+                      block_table=case.block_table, block_size=case.block_size)
+    kc = np.stack([O.gather_paged(case.k, case.block_table[b], 4, case.seq_kv) for b in range(2)])
+    vc = np.stack([O.gather_paged(case.v, case.block_table[b], 4, case.seq_kv) for b in range(2)])
+    contig = O.prefill(case.q, kc, vc, 4, 2, case.seq_kv, case.position_offset, case.scale)
+    assert np.array_equal(paged, contig)
+    rows = O.prefill(case.q, kc, vc, 4, 2, case.seq_kv, case.position_offset, case.scale,
+                     rows=[0, 5, 10])
+    np.testing.assert_allclose(rows, contig[:, [0, 5, 10]], rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------- brute
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_agrees(seed):
+    rng = np.random.default_rng(100 + seed)
+    H = int(rng.choice([1, 2, 4, 6]))
+    divs = [d for d in range(1, H + 1) if H % d == 0]
+    Hkv = int(rng.choice(divs))
+    D = int(rng.choice([1, 3, 8]))
+    sq = int(rng.integers(1, 6))
+    off = int(rng.integers(0, 5))
+    skv = off + sq + int(rng.integers(-min(off, 2), 3))   # also seq_kv != off + seq_q
+    skv = max(skv, 1)
+    q = rng.standard_normal((sq, H, D))
+    k = rng.standard_normal((skv, Hkv, D))
+    v = rng.standard_normal((skv, Hkv, D))
+    scale = float(rng.uniform(0.1, 2.0))
+    got = O.gqa_attention(q, k, v, H, Hkv, off, scale)
+    ref = np.array(brute.gqa_attention(q.tolist(), k.tolist(), v.tolist(), H, Hkv, off, scale))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_oracle_rejects_bad_head_counts():
+    q = np.zeros((1, 3, 2))
+    kv = np.zeros((1, 2, 2))
+    with pytest.raises(ValueError):
+        O.gqa_attention(q, kv, kv, 3, 2, 0, 1.0)
+    with pytest.raises(ValueError):
+        O.gqa_attention(q, np.zeros((1, 0, 2)), np.zeros((1, 0, 2)), 3, 0, 0, 1.0)
+
+
+# ----------------------------------------------------------------------- MLA
+
+def test_mla_absorbed_equals_naive():
+    rng = np.random.default_rng(21)
+    H, R, P, nope, vdim, L = 4, 16, 8, 8, 8, 13
+    q = rng.standard_normal((H, nope + P))
+    c = rng.standard_normal((L, R))
+    k_rot = rng.standard_normal((L, P))
+    w_uk = rng.standard_normal((H, nope, R)) * 0.3
+    w_uv = rng.standard_normal((H, vdim, R)) * 0.3
+    scale = 1.0 / math.sqrt(nope + P)
+    naive = O.mla_naive(q, c, k_rot, w_uk, w_uv, scale)
+    absorbed = O.mla_absorbed(q, c, k_rot, w_uk, w_uv, scale)
+    np.testing.assert_allclose(absorbed, naive, rtol=0, atol=1e-12)
+
+
+def test_mla_latent_matches_torch_sdpa_mqa():
+    rng = np.random.default_rng(22)
+    B, H, R, P, cap = 2, 8, 24, 8, 19
+    q = rng.standard_normal((B, H, R + P))
+    lat = rng.standard_normal((B, cap, R + P))
+    lens = [19, 7]
+    got = O.mla_decode_latent(q, lat, lens, R, 0.2)
+    for b, L in enumerate(lens):
+        tq = torch.from_numpy(q[b])[None, :, None, :]               # [1,H,1,R+P]
+        tk = torch.from_numpy(lat[b, :L])[None, None]               # [1,1,L,R+P]
+        tv = torch.from_numpy(lat[b, :L, :R].copy())[None, None]    # [1,1,L,R]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.2,
+                                                               enable_gqa=True)[0, :, 0].numpy()
+        np.testing.assert_allclose(got[b], ref, rtol=0, atol=1e-12)
+
+
+def test_mla_value_is_the_leading_latent_slice():
+    # With a zero query every position weighs the same: o_lat is the mean of latent[:, :R].
+    rng = np.random.default_rng(23)
+    lat = rng.standard_normal((1, 6, 12))
+    out = O.mla_decode_latent(np.zeros((1, 3, 12)), lat, [6], 9, 0.5)
+    np.testing.assert_allclose(out[0], np.broadcast_to(lat[0, :, :9].mean(0), (3, 9)), atol=1e-14)
