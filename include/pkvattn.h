@@ -1,0 +1,197 @@
+/*
+ * pkvattn: causal grouped-query attention over a KV cache on MI355X (gfx950).
+ *
+ * Four operations, one entry point each:
+ *   attn_prefill        multi-token causal prefill, contiguous or paged K/V
+ *   attn_decode_contig  single-token decode over a contiguous cache
+ *   attn_decode_paged   single-token decode over a block-table paged cache
+ *   mla_decode_latent   absorbed multi-head latent attention decode
+ *
+ * What is computed (kopitiam-runtime 0.2.4, src/attention.rs, module doc
+ * "Grouped-query attention" and "Causal masking", fns repeat_kv_heads,
+ * causal_mask, attention_forward):
+ *   query head h reads KV head h / (n_heads / n_kv_heads); the query at
+ *   row i sits at absolute position position_offset + i and attends to keys
+ *   j = 0 .. position_offset + i (and j < seq_kv);
+ *   o[i,h,:] = sum_j softmax_j(attention_scale * q[i,h,:] . k[j,h/G,:]) v[j,h/G,:].
+ * attention_scale is the whole logit multiplier (kopitiam uses 1/sqrt(head_dim);
+ * frink-models 0.31.0 src/mla/mod.rs passes the scale explicitly).
+ * Decode is push-then-attend (frink-models 0.38.0 src/decoder/attn_block.rs,
+ * push_and_attend_row): the caller has already written this step's K/V, and
+ * the query of sequence b sits at position seq_lens[b] - 1.
+ *
+ * Conventions shared by every entry point:
+ *  - dtype is a pkva_dtype code. Inputs and outputs use it; accumulation and
+ *    softmax are always fp32. bf16 outputs are rounded to nearest even.
+ *  - All tensors are dense, row-major, token-major, in DEVICE memory, owned by
+ *    the caller. Index arrays (block_table, seq_lens) are device int32.
+ *    The library never allocates, frees or synchronises; work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and the call returns as
+ *    soon as it is enqueued.
+ *  - Host-side validation runs before any HIP call. On a non-zero return
+ *    nothing was enqueued. Return codes:
+ *      PKVA_OK           enqueued
+ *      PKVA_EINVAL       a required pointer is NULL, a size is out of range,
+ *                        n_kv_heads does not divide n_heads, the scale is not
+ *                        finite or is negative, ...
+ *      PKVA_EUNSUPPORTED dtype code unknown, or (dtype, head size) combination
+ *                        not built (see each entry point)
+ *      PKVA_EWORKSPACE   workspace NULL or smaller than the *_workspace_size call
+ *      PKVA_EHIP         the kernel launch failed
+ *  - Device-side data errors never cause an out-of-bounds access: a sequence
+ *    whose seq_lens entry is outside [1, max_seq_len], or whose block table
+ *    names a block outside [0, num_blocks) among the blocks it needs, gets
+ *    NaN in every output element of that sequence (prefill: of the affected
+ *    query rows' heads).
+ *  - Results are deterministic: the same inputs give bitwise-identical
+ *    outputs on every call, and attn_decode_contig and attn_decode_paged give
+ *    bitwise-identical outputs for the same cache rows (frink-models 0.38.0
+ *    src/decoder/attn_block.rs, doc of push_and_attend_row: paging changes
+ *    where rows live and nothing else).
+ *  - The library holds no mutable global state; calls are thread-safe.
+ *    Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef PKVATTN_H
+#define PKVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKVA_F32 = 0, PKVA_BF16 = 1 } pkva_dtype;
+
+enum {
+  PKVA_OK = 0,
+  PKVA_EINVAL = 1,
+  PKVA_EUNSUPPORTED = 2,
+  PKVA_EWORKSPACE = 3,
+  PKVA_EHIP = 4
+};
+
+/* A static, human-readable name for a return code ("unknown status" otherwise). */
+const char* pkva_status_string(int status);
+
+/* The library's version string, e.g. "pkvattn 0.1.0 gfx950". */
+const char* pkva_version(void);
+
+/*
+ * attn_prefill: causal GQA for a batch of sequences that share seq_q, seq_kv
+ * and position_offset (kopitiam-runtime 0.2.4 src/attention.rs,
+ * attention_forward and causal_mask; the same mask serves a prompt prefill,
+ * position_offset == 0, and a chunk after cached tokens).
+ *
+ *   q  [batch, seq_q, n_heads, head_dim]              (dtype)
+ *   o  [batch, seq_q, n_heads, head_dim]              (dtype, written)
+ *   Contiguous K/V (block_table == NULL):
+ *     k, v  [batch, kv_capacity, n_kv_heads, head_dim], rows 0..seq_kv-1 used;
+ *     requires seq_kv <= kv_capacity. max_blocks_per_seq, block_size and
+ *     num_blocks are ignored.
+ *   Paged K/V (block_table != NULL):
+ *     k, v  pools [num_blocks, block_size, n_kv_heads, head_dim];
+ *     block_table [batch, max_blocks_per_seq] int32; token t of sequence b is
+ *     row t % block_size of block block_table[b][t / block_size];
+ *     requires block_size a power of two and
+ *     seq_kv <= max_blocks_per_seq * block_size. kv_capacity is ignored.
+ *   Row i of q sits at absolute position position_offset + i and sees keys
+ *   0 .. min(position_offset + i, seq_kv - 1). Key 0 is always visible.
+ *   Requires batch, n_heads, n_kv_heads, seq_q, seq_kv >= 1,
+ *   n_heads % n_kv_heads == 0, position_offset >= 0.
+ *   Built: (PKVA_F32, head_dim 16), (PKVA_BF16, head_dim 128); others return
+ *   PKVA_EUNSUPPORTED.
+ */
+int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o,
+                 int batch, int n_heads, int n_kv_heads, int head_dim,
+                 int seq_q, int seq_kv, int position_offset, float attention_scale,
+                 const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                 int num_blocks, int kv_capacity, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_contig / attn_decode_paged need for
+ * these sizes (the split-K partial results). Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_size(int batch, int n_heads, int n_kv_heads, int head_dim,
+                                  int max_seq_len);
+
+/*
+ * attn_decode_contig: one query token per sequence over a contiguous cache
+ * (frink-models 0.38.0 src/decoder/attn_block.rs, push_and_attend_row,
+ * contiguous arm: push this row, then attend over every row the sequence
+ * holds).
+ *
+ *   q        [batch, n_heads, head_dim]                  (dtype)
+ *   k_cache, v_cache [batch, kv_capacity, n_kv_heads, head_dim] (dtype)
+ *   o        [batch, n_heads, head_dim]                  (dtype, written)
+ *   seq_lens [batch] int32, device: keys 0..seq_lens[b]-1 of sequence b,
+ *            including the query's own (already appended) key.
+ *   max_seq_len: host upper bound on every seq_lens[b]; sizes the launch.
+ *            Requires 1 <= max_seq_len <= kv_capacity.
+ *   workspace: device memory of at least attn_decode_workspace_size(...)
+ *            bytes, contents irrelevant on entry, clobbered on return.
+ *   Built: (PKVA_F32, 16), (PKVA_BF16, 128), with n_heads / n_kv_heads <= 16.
+ */
+int attn_decode_contig(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                       void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                       const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                       float attention_scale, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * attn_decode_paged: one query token per sequence over a block-table paged
+ * cache shared across sequences (frink-models 0.38.0
+ * src/decoder/attn_block.rs, push_and_attend_row, paged arm: attend through
+ * the sequence's block_table over seq_len keys).
+ *
+ *   q        [batch, n_heads, head_dim]                          (dtype)
+ *   k_pool, v_pool [num_blocks, block_size, n_kv_heads, head_dim] (dtype)
+ *   o        [batch, n_heads, head_dim]                          (dtype, written)
+ *   block_table [batch, max_blocks_per_seq] int32, device; token t of
+ *            sequence b is row t % block_size of block block_table[b][t / block_size].
+ *            Entries past the sequence's last needed block are never read.
+ *   seq_lens, max_seq_len, workspace: as attn_decode_contig; requires
+ *            max_seq_len <= max_blocks_per_seq * block_size and block_size a
+ *            power of two.
+ *   For the same rows, the result is bitwise identical to attn_decode_contig.
+ *   Built: as attn_decode_contig.
+ */
+int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* v_pool,
+                      void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                      const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                      int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                      float attention_scale, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Bytes of device workspace mla_decode_latent needs. Returns 0 for invalid sizes.
+ */
+size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seq_len);
+
+/*
+ * mla_decode_latent: absorbed multi-head latent attention decode
+ * (frink-models 0.31.0 src/mla/mod.rs, absorbed_attention and the MlaKvB
+ * doc): multi-query attention in which every head's key is the whole cached
+ * latent row [c | k_rot] (width kv_lora_rank + qk_rope_head_dim) and its
+ * value is the row's first kv_lora_rank entries.
+ *
+ *   q_abs   [batch, n_heads, kv_lora_rank + qk_rope_head_dim] (dtype): per head
+ *           the absorbed nope part (kv_lora_rank) then the rotated rope part.
+ *   latent  [batch, kv_capacity, kv_lora_rank + qk_rope_head_dim] (dtype).
+ *   o_lat   [batch, n_heads, kv_lora_rank] (dtype, written): the softmax-weighted
+ *           latent, before the per-head value up-projection.
+ *   seq_lens, max_seq_len, workspace: as attn_decode_contig (the latent row of
+ *           the current token is already appended).
+ *   Built: PKVA_BF16 with kv_lora_rank 512, qk_rope_head_dim 64.
+ */
+int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_lat,
+                      int batch, int n_heads, int kv_lora_rank, int qk_rope_head_dim,
+                      const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                      float attention_scale, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKVATTN_H */

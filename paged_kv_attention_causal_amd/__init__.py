@@ -1,0 +1,256 @@
+"""Python binding of libpkvattn: causal GQA prefill, contiguous/paged decode, MLA latent decode.
+
+Argument marshalling only. Every function takes torch tensors that already
+live on the GPU, checks that they are dense and of one supported dtype, reads
+their sizes, and calls the C entry point of the same name in
+``libpkvattn.so`` on the current torch stream. All arithmetic runs in the HIP
+kernels; there is no CPU path. If the library is missing, every call raises.
+
+The library is loaded after ``torch`` so that it binds to the HIP runtime
+torch already loaded (both name ``libamdhip64.so.7``), which makes torch's
+stream handles valid arguments.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+__all__ = [
+    "PkvaError",
+    "library_path",
+    "lib",
+    "header_symbols",
+    "attn_prefill",
+    "attn_decode_contig",
+    "attn_decode_paged",
+    "attn_decode_workspace_size",
+    "mla_decode_latent",
+    "mla_decode_workspace_size",
+    "status_string",
+    "F32",
+    "BF16",
+]
+
+F32 = 0
+BF16 = 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkvattn.h")
+_LIB = None
+
+
+class PkvaError(RuntimeError):
+    """A non-zero status from the library; ``.status`` holds the code."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpkvattn.so")
+
+
+def lib():
+    """The loaded ``libpkvattn.so`` (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        import torch  # noqa: F401  -- bind to torch's HIP runtime first
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m paged_kv_attention_causal_amd.csrc.build`")
+        L = ctypes.CDLL(path)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.pkva_status_string.restype = ctypes.c_char_p
+        L.pkva_status_string.argtypes = [i32]
+        L.pkva_version.restype = ctypes.c_char_p
+        L.pkva_version.argtypes = []
+        L.attn_prefill.restype = i32
+        L.attn_prefill.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                   vp, i32, i32, i32, i32, vp]
+        L.attn_decode_workspace_size.restype = sz
+        L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.attn_decode_contig.restype = i32
+        L.attn_decode_contig.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, f32,
+                                         vp, sz, vp]
+        L.attn_decode_paged.restype = i32
+        L.attn_decode_paged.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, i32,
+                                        vp, i32, f32, vp, sz, vp]
+        L.mla_decode_workspace_size.restype = sz
+        L.mla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mla_decode_latent.restype = i32
+        L.mla_decode_latent.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, f32,
+                                        vp, sz, vp]
+        _LIB = L
+    return _LIB
+
+
+def header_symbols() -> list:
+    """Names of the functions ``include/pkvattn.h`` declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().pkva_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - the library itself is missing
+        return "unknown"
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PkvaError(fn, status)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _stream(t, stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _i32(t, name):
+    import torch
+    _dev(t, name)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def attn_prefill(q, k, v, *, seq_kv: int, position_offset: int, attention_scale: float,
+                 block_table=None, block_size: int = 0, out=None, stream=None):
+    """Causal GQA prefill; returns ``o`` ``[B, seq_q, H, D]`` (see ``attn_prefill`` in pkvattn.h).
+
+    Contiguous: ``k``/``v`` are ``[B, kv_capacity, Hkv, D]``. Paged: ``k``/``v`` are pools
+    ``[num_blocks, block_size, Hkv, D]`` and ``block_table`` is int32 ``[B, max_blocks]``.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != v.shape:
+        raise ValueError("q, k, v must share a dtype and k, v a shape")
+    B, seq_q, H, D = q.shape
+    Hkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    if block_table is not None:
+        _i32(block_table, "block_table")
+        nb, bs = k.shape[0], k.shape[1]
+        if block_size and block_size != bs:
+            raise ValueError("block_size disagrees with the pool shape")
+        st = lib().attn_prefill(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, D,
+                                seq_q, seq_kv, position_offset, attention_scale,
+                                _ptr(block_table), block_table.shape[1], bs, nb, 0,
+                                _stream(q, stream))
+    else:
+        st = lib().attn_prefill(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, D,
+                                seq_q, seq_kv, position_offset, attention_scale, None, 0, 0, 0,
+                                k.shape[1], _stream(q, stream))
+    _check("attn_prefill", st)
+    return out
+
+
+def attn_decode_workspace_size(batch, n_heads, n_kv_heads, head_dim, max_seq_len) -> int:
+    return int(lib().attn_decode_workspace_size(batch, n_heads, n_kv_heads, head_dim, max_seq_len))
+
+
+def _workspace(nbytes, like, workspace):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=like.device)
+    _dev(workspace, "workspace")
+    return workspace
+
+
+def attn_decode_contig(q, k_cache, v_cache, seq_lens, *, max_seq_len: int, attention_scale: float,
+                       out=None, workspace=None, stream=None):
+    """Single-token decode over ``[B, capacity, Hkv, D]`` caches; returns ``o`` ``[B, H, D]``."""
+    import torch
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    _i32(seq_lens, "seq_lens")
+    B, H, D = q.shape
+    Hkv = k_cache.shape[2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out")
+    nbytes = attn_decode_workspace_size(B, H, Hkv, D, max_seq_len)
+    workspace = _workspace(nbytes, q, workspace)
+    st = lib().attn_decode_contig(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                  B, H, Hkv, D, _ptr(seq_lens), k_cache.shape[1], max_seq_len,
+                                  attention_scale, _ptr(workspace), workspace.numel(),
+                                  _stream(q, stream))
+    _check("attn_decode_contig", st)
+    return out
+
+
+def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, max_seq_len: int,
+                      attention_scale: float, out=None, workspace=None, stream=None):
+    """Single-token decode over ``[num_blocks, block_size, Hkv, D]`` pools; returns ``[B, H, D]``."""
+    import torch
+    for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _dev(t, n)
+    _i32(block_table, "block_table")
+    _i32(seq_lens, "seq_lens")
+    B, H, D = q.shape
+    nb, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out")
+    nbytes = attn_decode_workspace_size(B, H, Hkv, D, max_seq_len)
+    workspace = _workspace(nbytes, q, workspace)
+    st = lib().attn_decode_paged(_dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                                 B, H, Hkv, D, _ptr(block_table), block_table.shape[1], bs, nb,
+                                 _ptr(seq_lens), max_seq_len, attention_scale, _ptr(workspace),
+                                 workspace.numel(), _stream(q, stream))
+    _check("attn_decode_paged", st)
+    return out
+
+
+def mla_decode_workspace_size(batch, n_heads, kv_lora_rank, max_seq_len) -> int:
+    return int(lib().mla_decode_workspace_size(batch, n_heads, kv_lora_rank, max_seq_len))
+
+
+def mla_decode_latent(q_abs, latent, seq_lens, *, kv_lora_rank: int, max_seq_len: int,
+                      attention_scale: float, out=None, workspace=None, stream=None):
+    """Absorbed MLA decode; ``q_abs`` ``[B, H, R+P]``, ``latent`` ``[B, cap, R+P]`` -> ``[B, H, R]``."""
+    import torch
+    _dev(q_abs, "q_abs")
+    _dev(latent, "latent")
+    _i32(seq_lens, "seq_lens")
+    B, H, W = q_abs.shape
+    P = W - kv_lora_rank
+    if out is None:
+        out = torch.empty((B, H, kv_lora_rank), dtype=q_abs.dtype, device=q_abs.device)
+    _dev(out, "out")
+    nbytes = mla_decode_workspace_size(B, H, kv_lora_rank, max_seq_len)
+    workspace = _workspace(nbytes, q_abs, workspace)
+    st = lib().mla_decode_latent(_dtype_code(q_abs), _ptr(q_abs), _ptr(latent), _ptr(out), B, H,
+                                 kv_lora_rank, P, _ptr(seq_lens), latent.shape[1], max_seq_len,
+                                 attention_scale, _ptr(workspace), workspace.numel(),
+                                 _stream(q_abs, stream))
+    _check("mla_decode_latent", st)
+    return out

@@ -1,0 +1,264 @@
+// C-ABI entry points: argument validation, workspace sizing and kernel
+// dispatch. Every check runs on the host before the first HIP call, so a
+// rejected call enqueues nothing (and the checks run without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pkvattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kPrefillThreads = 256;
+constexpr int kDecodeGroupMax = 8;        // largest n_heads / n_kv_heads the decode kernel packs
+constexpr int kMlaTargetGroups = 256;     // workgroups that fill the 256 compute units
+constexpr int64_t kMaxGrid = INT_MAX;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool scale_ok(float s) { return std::isfinite(s) && s >= 0.0f; }
+
+bool heads_ok(int n_heads, int n_kv_heads, int head_dim) {
+  return n_heads >= 1 && n_kv_heads >= 1 && head_dim >= 1 && n_heads % n_kv_heads == 0;
+}
+
+bool dtype_known(int dtype) { return dtype == PKVA_F32 || dtype == PKVA_BF16; }
+
+// Largest power of two that divides n.
+int pow2_divisor(int n) { return n & (-n); }
+
+struct DecodeShape {
+  int gmax, kvs, nslab, max_chunks;
+  size_t ws_bytes;
+};
+
+// Decode launch shape. Depends only on sizes, never on the cache layout, so
+// the contiguous and paged entry points split the work identically.
+int decode_shape(int dtype, int batch, int n_heads, int n_kv_heads, int head_dim, int max_seq_len,
+                 DecodeShape* out) {
+  const int group = n_heads / n_kv_heads;
+  if (group > kDecodeGroupMax) return PKVA_EUNSUPPORTED;
+  out->gmax = next_pow2(group);
+  const int lanes = pkva::decode_lanes_per_row(dtype == PKVA_BF16, head_dim);
+  const int ngroups = kPrefillThreads / lanes;
+  int kvs = pow2_divisor(n_kv_heads);
+  if (kvs > ngroups) kvs = ngroups;
+  while (kvs * out->gmax > pkva::decode_heads_per_slab_max()) kvs /= 2;
+  out->kvs = kvs;
+  out->nslab = n_kv_heads / kvs;
+  out->max_chunks = (int)ceil_div(max_seq_len, pkva::decode_chunk_tokens());
+  const int64_t parts = (int64_t)batch * out->max_chunks * n_heads;
+  out->ws_bytes = (size_t)(parts * (head_dim + 2) * (int64_t)sizeof(float));
+  if ((int64_t)out->max_chunks > kMaxGrid || (int64_t)batch * out->nslab > 65535) return PKVA_EINVAL;
+  return PKVA_OK;
+}
+
+size_t decode_ws_bytes(int batch, int n_heads, int head_dim, int max_seq_len) {
+  const int64_t chunks = ceil_div(max_seq_len, pkva::decode_chunk_tokens());
+  return (size_t)((int64_t)batch * chunks * n_heads * (head_dim + 2) * (int64_t)sizeof(float));
+}
+
+struct MlaShape {
+  int nsplit, split_tokens;
+  size_t ws_bytes;
+};
+
+MlaShape mla_shape(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
+  MlaShape s;
+  const int tile = pkva::mla_tile_tokens();
+  const int64_t items = (int64_t)batch * (n_heads / pkva::mla_heads_per_group());
+  int64_t nsplit = items >= kMlaTargetGroups ? 1 : ceil_div(kMlaTargetGroups, items);
+  const int64_t max_split = ceil_div(max_seq_len, tile);
+  if (nsplit > max_split) nsplit = max_split;
+  if (nsplit < 1) nsplit = 1;
+  const int64_t per = ceil_div(ceil_div(max_seq_len, nsplit), tile) * tile;
+  s.split_tokens = (int)per;
+  s.nsplit = (int)ceil_div(max_seq_len, per);
+  s.ws_bytes = s.nsplit > 1
+                   ? (size_t)((int64_t)batch * s.nsplit * n_heads * (kv_lora_rank + 2) * (int64_t)sizeof(float))
+                   : 0;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkva_status_string(int status) {
+  switch (status) {
+    case PKVA_OK: return "ok";
+    case PKVA_EINVAL: return "invalid argument";
+    case PKVA_EUNSUPPORTED: return "unsupported dtype or size";
+    case PKVA_EWORKSPACE: return "workspace missing or too small";
+    case PKVA_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* pkva_version(void) { return "pkvattn 0.1.0 gfx950"; }
+
+int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o, int batch,
+                 int n_heads, int n_kv_heads, int head_dim, int seq_q, int seq_kv,
+                 int position_offset, float attention_scale, const int32_t* block_table,
+                 int max_blocks_per_seq, int block_size, int num_blocks, int kv_capacity,
+                 void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!q || !k || !v || !o) return PKVA_EINVAL;
+  if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim)) return PKVA_EINVAL;
+  if (seq_q < 1 || seq_kv < 1 || position_offset < 0) return PKVA_EINVAL;
+  if ((int64_t)position_offset + seq_q > INT_MAX / 2) return PKVA_EINVAL;
+  if (!scale_ok(attention_scale)) return PKVA_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
+    if ((int64_t)max_blocks_per_seq * block_size < seq_kv) return PKVA_EINVAL;
+  } else {
+    if (kv_capacity < seq_kv) return PKVA_EINVAL;
+  }
+  const bool bf16 = dtype == PKVA_BF16;
+  if (!pkva::prefill_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
+  const int64_t q_tiles = ceil_div(seq_q, pkva::prefill_block_m());
+  if (q_tiles * batch * n_heads > kMaxGrid) return PKVA_EINVAL;
+
+  pkva::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o;
+  p.block_table = block_table;
+  p.batch = batch; p.n_heads = n_heads; p.n_kv_heads = n_kv_heads;
+  p.group = n_heads / n_kv_heads;
+  p.seq_q = seq_q; p.seq_kv = seq_kv; p.position_offset = position_offset;
+  p.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  p.block_shift = paged ? log2i(block_size) : 0;
+  p.num_blocks = paged ? num_blocks : 0;
+  p.kv_capacity = paged ? 0 : kv_capacity;
+  p.q_tiles = (int)q_tiles;
+  p.scale_log2 = attention_scale * pkva::kLog2eHost;
+  const int rc = pkva::launch_prefill(bf16, paged, head_dim, p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
+}
+
+size_t attn_decode_workspace_size(int batch, int n_heads, int n_kv_heads, int head_dim,
+                                  int max_seq_len) {
+  if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim) || max_seq_len < 1) return 0;
+  return decode_ws_bytes(batch, n_heads, head_dim, max_seq_len);
+}
+
+static int decode_common(int dtype, bool paged, const void* q, const void* k, const void* v,
+                         void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                         const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                         int num_blocks, const int32_t* seq_lens, int kv_capacity,
+                         int max_seq_len, float attention_scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!q || !k || !v || !o || !seq_lens) return PKVA_EINVAL;
+  if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim) || max_seq_len < 1) return PKVA_EINVAL;
+  if (!scale_ok(attention_scale)) return PKVA_EINVAL;
+  if (paged) {
+    if (!block_table) return PKVA_EINVAL;
+    if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
+    if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKVA_EINVAL;
+  } else {
+    if (kv_capacity < max_seq_len) return PKVA_EINVAL;
+  }
+  const bool bf16 = dtype == PKVA_BF16;
+  if (!pkva::decode_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
+  DecodeShape sh;
+  const int rc0 = decode_shape(dtype, batch, n_heads, n_kv_heads, head_dim, max_seq_len, &sh);
+  if (rc0 != PKVA_OK) return rc0;
+  if (!workspace || workspace_bytes < sh.ws_bytes) return PKVA_EWORKSPACE;
+  if (((uintptr_t)workspace & 15u) != 0) return PKVA_EWORKSPACE;
+
+  pkva::DecodeParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o;
+  p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.ws_o = (float*)workspace;
+  p.ws_ml = p.ws_o + (int64_t)batch * sh.max_chunks * n_heads * head_dim;
+  p.batch = batch; p.n_heads = n_heads; p.n_kv_heads = n_kv_heads;
+  p.group = n_heads / n_kv_heads;
+  p.kvs = sh.kvs; p.nslab = sh.nslab; p.max_chunks = sh.max_chunks;
+  p.max_seq_len = max_seq_len;
+  p.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  p.block_shift = paged ? log2i(block_size) : 0;
+  p.num_blocks = paged ? num_blocks : 0;
+  p.kv_capacity = paged ? 0 : kv_capacity;
+  p.scale_log2 = attention_scale * pkva::kLog2eHost;
+  const int rc = pkva::launch_decode(bf16, paged, head_dim, sh.gmax, p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
+}
+
+int attn_decode_contig(int dtype, const void* q, const void* k_cache, const void* v_cache, void* o,
+                       int batch, int n_heads, int n_kv_heads, int head_dim,
+                       const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                       float attention_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return decode_common(dtype, false, q, k_cache, v_cache, o, batch, n_heads, n_kv_heads, head_dim,
+                       nullptr, 0, 0, 0, seq_lens, kv_capacity, max_seq_len, attention_scale,
+                       workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* v_pool, void* o,
+                      int batch, int n_heads, int n_kv_heads, int head_dim,
+                      const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                      int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                      float attention_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_common(dtype, true, q, k_pool, v_pool, o, batch, n_heads, n_kv_heads, head_dim,
+                       block_table, max_blocks_per_seq, block_size, num_blocks, seq_lens, 0,
+                       max_seq_len, attention_scale, workspace, workspace_bytes, stream);
+}
+
+size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
+  if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || max_seq_len < 1) return 0;
+  if (n_heads % pkva::mla_heads_per_group() != 0) return 0;
+  return mla_shape(batch, n_heads, kv_lora_rank, max_seq_len).ws_bytes;
+}
+
+int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_lat, int batch,
+                      int n_heads, int kv_lora_rank, int qk_rope_head_dim,
+                      const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                      float attention_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!q_abs || !latent || !o_lat || !seq_lens) return PKVA_EINVAL;
+  if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || qk_rope_head_dim < 0) return PKVA_EINVAL;
+  if (max_seq_len < 1 || kv_capacity < max_seq_len) return PKVA_EINVAL;
+  if (!scale_ok(attention_scale)) return PKVA_EINVAL;
+  if (!pkva::mla_supported(dtype == PKVA_BF16, kv_lora_rank, qk_rope_head_dim, n_heads))
+    return PKVA_EUNSUPPORTED;
+  const MlaShape sh = mla_shape(batch, n_heads, kv_lora_rank, max_seq_len);
+  if ((int64_t)batch * (n_heads / pkva::mla_heads_per_group()) * sh.nsplit > kMaxGrid)
+    return PKVA_EINVAL;
+  if (sh.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < sh.ws_bytes) return PKVA_EWORKSPACE;
+    if (((uintptr_t)workspace & 15u) != 0) return PKVA_EWORKSPACE;
+  }
+
+  pkva::MlaParams p{};
+  p.q = q_abs; p.latent = latent; p.o = o_lat; p.seq_lens = seq_lens;
+  p.ws_o = (float*)workspace;
+  p.ws_ml = sh.ws_bytes > 0 ? p.ws_o + (int64_t)batch * sh.nsplit * n_heads * kv_lora_rank : nullptr;
+  p.batch = batch; p.n_heads = n_heads; p.kv_capacity = kv_capacity; p.max_seq_len = max_seq_len;
+  p.nsplit = sh.nsplit; p.split_tokens = sh.split_tokens;
+  p.scale_log2 = attention_scale * pkva::kLog2eHost;
+  const int rc = pkva::launch_mla(p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : PKVA_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, bf16
+// packing, wave64 lane exchanges through DPP, and the launch-side status codes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace pkva {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even) packed low|high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Dot product of two packed bf16 pairs, accumulated into c in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ------------------------------------------------------- lane exchanges
+// Value of the partner lane whose index differs from ours in bit BIT (and
+// possibly in lower bits). BIT 0..3 stay inside a 16-lane DPP row:
+//   bit 0: quad_perm [1,0,3,2]   (lane ^ 1)
+//   bit 1: quad_perm [2,3,0,1]   (lane ^ 2)
+//   bit 2: row_half_mirror       (lane ^ 7 inside each 8-lane half row)
+//   bit 3: row_mirror            (lane ^ 15 inside each 16-lane row)
+// The masks {1, 2, 7, 15} are linearly independent over GF(2), so a
+// butterfly over them covers every lane of a 16-lane group exactly once.
+// Bits 4 and 5 use a cross-row permute (lane ^ 16, lane ^ 32).
+template <int BIT>
+__device__ __forceinline__ float xchg(float x) {
+  static_assert(BIT >= 0 && BIT <= 5, "lane bit out of range");
+  const int xi = __float_as_int(x);
+  if constexpr (BIT == 0) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (BIT == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (BIT == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false));
+  } else if constexpr (BIT == 3) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x140, 0xF, 0xF, false));
+  } else if constexpr (BIT == 4) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 16u) << 2), xi));
+  } else {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), xi));
+  }
+}
+
+template <int N>
+struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };
+template <>
+struct Log2<1> { static constexpr int value = 0; };
+
+// Reduce-scatter of N partial sums across an aligned group of LG lanes.
+// On return lane `li` (index inside the group) holds in v[0..NV) the full
+// group sums of heads  (li / max(1, LG/N)) * NV + i,  NV = max(1, N/LG).
+template <int N, int BIT, int n>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[N], int li) {
+  if constexpr (BIT >= 0) {
+    if constexpr (n > 1) {
+      constexpr int half = n / 2;
+      const bool up = (li >> BIT) & 1;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float send = up ? v[i] : v[i + half];
+        const float keep = up ? v[i + half] : v[i];
+        v[i] = keep + xchg<BIT>(send);
+      }
+      reduce_scatter_step<N, BIT - 1, half>(v, li);
+    } else {
+      v[0] += xchg<BIT>(v[0]);
+      reduce_scatter_step<N, BIT - 1, 1>(v, li);
+    }
+  }
+}
+
+template <int LG, int N>
+__device__ __forceinline__ void reduce_scatter(float (&v)[N], int li) {
+  reduce_scatter_step<N, Log2<LG>::value - 1, N>(v, li);
+}
+
+// Wave64-wide max and sum (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, xchg<0>(x));
+  x = fmaxf(x, xchg<1>(x));
+  x = fmaxf(x, xchg<2>(x));
+  x = fmaxf(x, xchg<3>(x));
+  x = fmaxf(x, xchg<4>(x));
+  x = fmaxf(x, xchg<5>(x));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += xchg<0>(x);
+  x += xchg<1>(x);
+  x += xchg<2>(x);
+  x += xchg<3>(x);
+  x += xchg<4>(x);
+  x += xchg<5>(x);
+  return x;
+}
+
+}  // namespace pkva

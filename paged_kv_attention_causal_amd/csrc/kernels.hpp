@@ -1,0 +1,77 @@
+// Launch-side parameter blocks and launchers of the HIP kernels. Validation
+// happens in the C-ABI layer before any of these is called; the launchers
+// assume sizes and pointers are already checked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkva {
+
+enum Status { kOk = 0, kEinval = 1, kEunsupported = 2, kEworkspace = 3, kEhip = 4 };
+
+// log2(e): the kernels run the softmax as exp2((s - m) * scale * log2(e)).
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct DecodeParams {
+  const void* q;              // [batch, n_heads, D]
+  const void* k;              // contiguous [batch, cap, Hkv, D] or pool [nb, bs, Hkv, D]
+  const void* v;
+  void* o;                    // [batch, n_heads, D]
+  const int32_t* seq_lens;    // [batch]
+  const int32_t* block_table; // [batch, max_blocks_per_seq] (paged)
+  float* ws_o;                // [batch, nslab, max_chunks, HS, D] partial outputs
+  float* ws_ml;               // [batch, nslab, max_chunks, HS, 2] (m * scale * log2e, l)
+  int batch, n_heads, n_kv_heads, group;
+  int kvs;                    // KV heads per workgroup slab
+  int nslab;                  // n_kv_heads / kvs
+  int max_chunks;
+  int max_seq_len;
+  int max_blocks_per_seq, block_shift, num_blocks;
+  int kv_capacity;
+  float scale_log2;           // attention_scale * log2(e)
+};
+
+int decode_chunk_tokens();
+int decode_heads_per_slab_max();
+bool decode_supported(bool bf16, int head_dim);
+int decode_lanes_per_row(bool bf16, int head_dim);
+int launch_decode(bool bf16, bool paged, int head_dim, int gmax, const DecodeParams& p,
+                  hipStream_t stream);
+
+struct PrefillParams {
+  const void* q;              // [batch, seq_q, n_heads, D]
+  const void* k;              // contiguous [batch, cap, Hkv, D] or pool [nb, bs, Hkv, D]
+  const void* v;
+  void* o;                    // [batch, seq_q, n_heads, D]
+  const int32_t* block_table; // [batch, max_blocks_per_seq] (paged)
+  int batch, n_heads, n_kv_heads, group;
+  int seq_q, seq_kv, position_offset;
+  int max_blocks_per_seq, block_shift, num_blocks;
+  int kv_capacity;
+  int q_tiles;                // ceil(seq_q / BLOCK_M)
+  float scale_log2;
+};
+
+bool prefill_supported(bool bf16, int head_dim);
+int prefill_block_m();
+int launch_prefill(bool bf16, bool paged, int head_dim, const PrefillParams& p, hipStream_t stream);
+
+struct MlaParams {
+  const void* q;              // [batch, n_heads, R + P]
+  const void* latent;         // [batch, cap, R + P]
+  void* o;                    // [batch, n_heads, R]
+  const int32_t* seq_lens;
+  float* ws_o;                // [batch, nsplit, n_heads, R]   (nsplit > 1 only)
+  float* ws_ml;               // [batch, nsplit, n_heads, 2]
+  int batch, n_heads, kv_capacity, max_seq_len;
+  int nsplit, split_tokens;   // context split: nsplit pieces of split_tokens tokens
+  float scale_log2;
+};
+
+bool mla_supported(bool bf16, int kv_lora_rank, int rope_dim, int n_heads);
+int mla_heads_per_group();
+int mla_tile_tokens();
+int launch_mla(const MlaParams& p, hipStream_t stream);
+
+}  // namespace pkva

@@ -1,0 +1,164 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares, and rejects
+bad arguments before any HIP call (so no GPU is needed and nothing is launched)."""
+import ctypes
+
+import pytest
+
+import paged_kv_attention_causal_amd as pk
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+P = ctypes.c_void_p(4096)     # a non-null pointer that is never dereferenced
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return pk.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = pk.header_symbols()
+    assert {"attn_prefill", "attn_decode_contig", "attn_decode_paged", "mla_decode_latent",
+            "attn_decode_workspace_size", "mla_decode_workspace_size", "pkva_status_string",
+            "pkva_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.pkva_version().decode().startswith("pkvattn")
+    assert L.pkva_status_string(0) == b"ok"
+    assert L.pkva_status_string(2) == b"unsupported dtype or size"
+    assert L.pkva_status_string(99) == b"unknown status"
+
+
+def _prefill(L, **kw):
+    a = dict(dtype=1, q=P, k=P, v=P, o=P, batch=1, n_heads=28, n_kv_heads=4, head_dim=128,
+             seq_q=64, seq_kv=64, off=0, scale=0.088, bt=NULL, maxb=0, bs=0, nb=0, cap=64)
+    a.update(kw)
+    return L.attn_prefill(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["batch"], a["n_heads"],
+                          a["n_kv_heads"], a["head_dim"], a["seq_q"], a["seq_kv"], a["off"],
+                          a["scale"], a["bt"], a["maxb"], a["bs"], a["nb"], a["cap"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), EUNSUP),               # not fp32/bf16: rejected like a non-f32 input
+    (dict(dtype=-1), EUNSUP),
+    (dict(q=NULL), EINVAL),
+    (dict(o=NULL), EINVAL),
+    (dict(n_kv_heads=3), EINVAL),          # does not divide n_heads
+    (dict(n_kv_heads=0), EINVAL),
+    (dict(n_heads=0), EINVAL),
+    (dict(batch=0), EINVAL),
+    (dict(seq_q=0), EINVAL),
+    (dict(seq_kv=0), EINVAL),
+    (dict(off=-1), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(scale=float("inf")), EINVAL),
+    (dict(scale=-0.5), EINVAL),
+    (dict(cap=63), EINVAL),                # contiguous cache shorter than seq_kv
+    (dict(bt=P, maxb=4, bs=12, nb=10), EINVAL),   # block size not a power of two
+    (dict(bt=P, maxb=3, bs=16, nb=10), EINVAL),   # table too short for seq_kv
+    (dict(bt=P, maxb=4, bs=16, nb=0), EINVAL),
+    (dict(head_dim=64), EUNSUP),           # not built
+    (dict(dtype=0, head_dim=128), EUNSUP),
+    (dict(dtype=1, head_dim=16), EUNSUP),
+])
+def test_prefill_validation(L, kw, code):
+    assert _prefill(L, **kw) == code
+
+
+def _decode(L, paged, **kw):
+    a = dict(dtype=1, q=P, k=P, v=P, o=P, batch=4, n_heads=32, n_kv_heads=8, head_dim=128,
+             bt=P, maxb=8, bs=16, nb=100, lens=P, cap=128, maxlen=128, scale=0.088,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    if paged:
+        return L.attn_decode_paged(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["batch"],
+                                   a["n_heads"], a["n_kv_heads"], a["head_dim"], a["bt"], a["maxb"],
+                                   a["bs"], a["nb"], a["lens"], a["maxlen"], a["scale"], a["ws"],
+                                   a["wsb"], NULL)
+    return L.attn_decode_contig(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["batch"],
+                                a["n_heads"], a["n_kv_heads"], a["head_dim"], a["lens"], a["cap"],
+                                a["maxlen"], a["scale"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), EUNSUP),
+    (dict(lens=NULL), EINVAL),
+    (dict(k=NULL), EINVAL),
+    (dict(maxlen=0), EINVAL),
+    (dict(n_kv_heads=5), EINVAL),
+    (dict(n_heads=64, n_kv_heads=4), EUNSUP),     # group of 16 is not packed
+    (dict(head_dim=96), EUNSUP),
+    (dict(ws=NULL), EWS),
+    (dict(wsb=16), EWS),
+    (dict(ws=ctypes.c_void_p(4100)), EWS),        # workspace not 16-byte aligned
+    (dict(scale=float("nan")), EINVAL),
+])
+def test_decode_validation(L, paged, kw, code):
+    assert _decode(L, paged, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=NULL), EINVAL),
+    (dict(bs=24), EINVAL),
+    (dict(maxb=7), EINVAL),        # 7 * 16 < max_seq_len 128
+    (dict(nb=0), EINVAL),
+])
+def test_paged_decode_table_validation(L, kw, code):
+    assert _decode(L, True, **kw) == code
+
+
+def test_contig_decode_capacity_validation(L):
+    assert _decode(L, False, cap=127) == EINVAL
+
+
+def test_decode_workspace_size_formula(L):
+    # chunks of 256 tokens; per (sequence, chunk, head): head_dim + 2 floats
+    assert L.attn_decode_workspace_size(64, 32, 8, 128, 8192) == 64 * 32 * 32 * 130 * 4
+    assert L.attn_decode_workspace_size(1, 4, 2, 16, 72) == 1 * 1 * 4 * 18 * 4
+    assert L.attn_decode_workspace_size(1, 4, 3, 16, 72) == 0     # invalid heads
+    assert L.attn_decode_workspace_size(0, 4, 2, 16, 72) == 0
+
+
+def _mla(L, **kw):
+    a = dict(dtype=1, q=P, lat=P, o=P, batch=32, n_heads=128, R=512, Pr=64, lens=P, cap=4096,
+             maxlen=4096, scale=0.072, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.mla_decode_latent(a["dtype"], a["q"], a["lat"], a["o"], a["batch"], a["n_heads"],
+                               a["R"], a["Pr"], a["lens"], a["cap"], a["maxlen"], a["scale"],
+                               a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), EUNSUP),
+    (dict(dtype=3), EUNSUP),
+    (dict(R=256), EUNSUP),
+    (dict(Pr=32), EUNSUP),
+    (dict(n_heads=120), EUNSUP),
+    (dict(q=NULL), EINVAL),
+    (dict(cap=100), EINVAL),
+    (dict(maxlen=0), EINVAL),
+    (dict(scale=-1.0), EINVAL),
+    (dict(batch=1, ws=NULL), EWS),         # small batch splits the context: needs a workspace
+])
+def test_mla_validation(L, kw, code):
+    assert _mla(L, **kw) == code
+
+
+def test_mla_workspace_size(L):
+    # 32 sequences x 8 head groups already fill 256 workgroups: no split, no workspace
+    assert L.mla_decode_workspace_size(32, 128, 512, 4096) == 0
+    # one sequence: 8 head groups, context split into ceil(256 / 8) = 32 pieces of 128 tokens
+    assert L.mla_decode_workspace_size(1, 128, 512, 4096) == 1 * 32 * 128 * 514 * 4
+    assert L.mla_decode_workspace_size(1, 100, 512, 4096) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 16)
+    with pytest.raises(ValueError):
+        pk.attn_decode_contig(q, torch.zeros(1, 8, 2, 16), torch.zeros(1, 8, 2, 16),
+                              torch.ones(1, dtype=torch.int32), max_seq_len=8, attention_scale=0.25)
