@@ -3,6 +3,7 @@
 // rejected call enqueues nothing (and the checks run without a GPU).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -45,12 +46,23 @@ bool dtype_known(int dtype) { return dtype == PKVA_F32 || dtype == PKVA_BF16; }
 int pow2_divisor(int n) { return n & (-n); }
 
 struct DecodeShape {
-  int gmax, kvs, nslab, max_chunks;
+  int gmax, kvs, nslab, n_ranges;
   size_t ws_bytes;
 };
 
-// Decode launch shape. Depends only on sizes, never on the cache layout, so
-// the contiguous and paged entry points split the work identically.
+// Upper bound on the equal token ranges the sequences are cut into (the
+// launcher lowers it to the resident workgroup slots); sizes the workspace.
+int decode_ranges(int batch, int max_seq_len) {
+  const int64_t by_tokens = ceil_div((int64_t)batch * max_seq_len, pkva::decode_min_tokens_per_range());
+  return (int)std::min<int64_t>(pkva::decode_max_ranges(), std::max<int64_t>(1, by_tokens));
+}
+
+size_t decode_ws_bytes(int batch, int n_heads, int head_dim, int max_seq_len) {
+  const int64_t slots = (int64_t)decode_ranges(batch, max_seq_len) + batch;
+  return (size_t)(slots * n_heads * (head_dim + 2) * (int64_t)sizeof(float) +
+                  (int64_t)(batch + 2) * (int64_t)sizeof(int32_t));
+}
+
 int decode_shape(int dtype, int batch, int n_heads, int n_kv_heads, int head_dim, int max_seq_len,
                  DecodeShape* out) {
   const int group = n_heads / n_kv_heads;
@@ -63,16 +75,10 @@ int decode_shape(int dtype, int batch, int n_heads, int n_kv_heads, int head_dim
   while (kvs * out->gmax > pkva::decode_heads_per_slab_max()) kvs /= 2;
   out->kvs = kvs;
   out->nslab = n_kv_heads / kvs;
-  out->max_chunks = (int)ceil_div(max_seq_len, pkva::decode_chunk_tokens());
-  const int64_t parts = (int64_t)batch * out->max_chunks * n_heads;
-  out->ws_bytes = (size_t)(parts * (head_dim + 2) * (int64_t)sizeof(float));
-  if ((int64_t)out->max_chunks > kMaxGrid || (int64_t)batch * out->nslab > 65535) return PKVA_EINVAL;
+  out->n_ranges = decode_ranges(batch, max_seq_len);
+  out->ws_bytes = decode_ws_bytes(batch, n_heads, head_dim, max_seq_len);
+  if (out->nslab > 65535) return PKVA_EINVAL;
   return PKVA_OK;
-}
-
-size_t decode_ws_bytes(int batch, int n_heads, int head_dim, int max_seq_len) {
-  const int64_t chunks = ceil_div(max_seq_len, pkva::decode_chunk_tokens());
-  return (size_t)((int64_t)batch * chunks * n_heads * (head_dim + 2) * (int64_t)sizeof(float));
 }
 
 struct MlaShape {
@@ -173,8 +179,10 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
     if (!block_table) return PKVA_EINVAL;
     if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
     if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKVA_EINVAL;
+    if ((int64_t)num_blocks * block_size > INT_MAX) return PKVA_EINVAL;   // pool rows index in 31 bits
   } else {
     if (kv_capacity < max_seq_len) return PKVA_EINVAL;
+    if ((int64_t)batch * kv_capacity > INT_MAX) return PKVA_EINVAL;       // cache rows index in 31 bits
   }
   const bool bf16 = dtype == PKVA_BF16;
   if (!pkva::decode_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
@@ -188,11 +196,14 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
   p.q = q; p.k = k; p.v = v; p.o = o;
   p.seq_lens = seq_lens;
   p.block_table = block_table;
+  const int64_t slots = (int64_t)sh.n_ranges + batch;
   p.ws_o = (float*)workspace;
-  p.ws_ml = p.ws_o + (int64_t)batch * sh.max_chunks * n_heads * head_dim;
+  p.ws_ml = p.ws_o + slots * n_heads * head_dim;
+  p.ws_cum = (int*)(p.ws_ml + slots * n_heads * 2);
   p.batch = batch; p.n_heads = n_heads; p.n_kv_heads = n_kv_heads;
   p.group = n_heads / n_kv_heads;
-  p.kvs = sh.kvs; p.nslab = sh.nslab; p.max_chunks = sh.max_chunks;
+  p.kvs = sh.kvs; p.nslab = sh.nslab; p.n_ranges = sh.n_ranges;
+  p.min_tokens_per_range = pkva::decode_min_tokens_per_range();
   p.max_seq_len = max_seq_len;
   p.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
   p.block_shift = paged ? log2i(block_size) : 0;

@@ -27,31 +27,34 @@ def hipcc():
     return "hipcc"
 
 
-def _compile(src):
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-x", "hip", "-c", os.path.join(HERE, src), "-o", obj]
+def _compile(src, objdir=OBJDIR, defines=()):
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + FLAGS + [f"-D{d}" for d in defines] + ["-x", "hip", "-c",
+                                                             os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj, r.stderr
 
 
-def build(verbose=False):
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose=False, out=OUT, defines=()):
+    """Compile every source and link ``out``; ``defines`` are extra -D macros (tuning knobs)."""
+    objdir = OBJDIR if out == OUT else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, objdir, defines), SOURCES))
     objs = [o for o, _ in results]
     if verbose:
         for (o, err) in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

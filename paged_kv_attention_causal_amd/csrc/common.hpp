@@ -95,6 +95,16 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[N], int li) {
   reduce_scatter_step<N, Log2<LG>::value - 1, N>(v, li);
 }
 
+// Sum over an aligned group of LG lanes (LG <= 16); every lane gets the same sum.
+template <int LG>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (LG >= 16) x += xchg<3>(x);
+  if constexpr (LG >= 8) x += xchg<2>(x);
+  if constexpr (LG >= 4) x += xchg<1>(x);
+  if constexpr (LG >= 2) x += xchg<0>(x);
+  return x;
+}
+
 // Wave64-wide max and sum (every lane gets the result).
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, xchg<0>(x));

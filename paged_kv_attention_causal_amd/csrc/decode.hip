@@ -6,20 +6,24 @@
 // push_and_attend_row). Query head h reads KV head h / G (kopitiam-runtime
 // 0.2.4 src/attention.rs, repeat_kv_heads).
 //
-// Split-K over the context. One workgroup owns a chunk of kDecChunk tokens
-// of one sequence and a slab of KV heads, with every query head of those KV
-// heads, so each K/V byte of the chunk is read from HBM exactly once:
-//   pass 1  stream the chunk's K rows; 16-byte lane loads, each lane group
-//           covers one (token, KV head) row; dot products with the group's
-//           G queries are reduced across the group with DPP exchanges and
-//           land in LDS as raw scores;
-//   pass 2  per head, exact softmax over the chunk in LDS (chunk max m,
-//           exp2, chunk sum l);
-//   pass 3  stream the chunk's V rows and accumulate p * v per lane, then
-//           reduce the token sub-rows through LDS in a fixed tree order.
-// The chunk's (m, l, O) go to the workspace; decode_combine merges the
-// chunks of a sequence in chunk order. Contiguous and paged differ only in
-// the row address, so their arithmetic, and their results, are identical.
+// Split-K over the context with a balanced partition: all sequences' tokens
+// are laid end to end and cut into equal ranges, one per workgroup, so every
+// workgroup streams the same number of K/V bytes whatever the length mix.
+// A workgroup owns its range for a slab of KV heads, with every query head
+// of those KV heads, so each K/V byte is read from HBM exactly once.
+//
+// Inside a workgroup every aligned group of lanes (16 for bf16 D=128) is an
+// independent worker for one KV head and one token stream (every R-th token
+// of the piece): it loads the K and V rows of U tokens at once (16 bytes per
+// lane), reduces q . k for its G query heads with a DPP butterfly so every
+// lane holds every score, and runs the online softmax for the batch in
+// registers (one rescale per batch). There is no barrier in the streaming
+// loop. At the end of a sequence's piece the token streams are merged
+// through LDS in a fixed tree order and the piece's (m, l, O) goes to
+// workspace slot (range index + sequence index), which is unique.
+// decode_combine merges a sequence's pieces in range order. Contiguous and
+// paged differ only in the row address, so their arithmetic, and their
+// results, are identical.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,9 +32,17 @@ namespace pkva {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDecChunk = 256;   // tokens per workgroup (the split-K unit)
 constexpr int kHsMax = 32;       // query heads per workgroup
-constexpr int kUnroll = 8;       // row loads in flight per lane
+#ifndef PKVA_DECODE_UNROLL
+#define PKVA_DECODE_UNROLL 2
+#endif
+constexpr int kUnroll = PKVA_DECODE_UNROLL;  // tokens per batch per lane group (K and V rows in flight)
+#ifndef PKVA_DECODE_WAVES_G4
+#define PKVA_DECODE_WAVES_G4 3
+#endif
+constexpr int kWavesG4 = PKVA_DECODE_WAVES_G4;  // waves per SIMD the group-of-4 kernels are built for
+constexpr int kBtWin = 1024;     // block-table entries cached in LDS per sub-piece
+constexpr float kLazy = 8.0f;    // log2 headroom before the running max is moved
 
 template <bool BF16>
 struct Lane16 {
@@ -71,276 +83,386 @@ __device__ __forceinline__ void unpack16(const uint4 w, float (&x)[Lane16<BF16>:
   }
 }
 
-// Element offset of row (token t, kv head kvh) of sequence b.
-template <bool PAGED>
-struct RowAddr {
-  const int* s_blk;  // paged: block ids of the chunk, s_blk[i] = block of (blk0 + i)
-  int blk0;
-  int64_t seq_base;  // contiguous: b * kv_capacity * row_stride
-  __device__ __forceinline__ int64_t operator()(int t, int shift, int64_t row_stride) const {
-    if constexpr (PAGED) {
-      const int bs_mask = (1 << shift) - 1;
-      const int64_t blk = s_blk[(t >> shift) - blk0];
-      return ((blk << shift) + (t & bs_mask)) * row_stride;
-    } else {
-      return seq_base + (int64_t)t * row_stride;
-    }
+// Inclusive scan of one value per thread across the workgroup (256 threads).
+__device__ __forceinline__ int block_scan(int x, int* s_tmp) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
-};
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += s_tmp[w];
+  __syncthreads();
+  return x + add;
+}
+
+__device__ __forceinline__ int valid_len(const DecodeParams& p, int b) {
+  const int L = p.seq_lens[b];
+  return (L >= 1 && L <= p.max_seq_len) ? L : 0;
+}
 
 template <bool BF16, int D, int GMAX, bool PAGED>
-__global__ __launch_bounds__(kThreads) void decode_partial(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4)) void decode_partial(DecodeParams p) {
   constexpr int E = Lane16<BF16>::E;
   constexpr int LG = D / E;          // lanes per (token, kv head) row
   constexpr int NG = kThreads / LG;  // lane groups per workgroup
-  constexpr int NV = GMAX > LG ? GMAX / LG : 1;
-  constexpr int LPH = LG > GMAX ? LG / GMAX : 1;  // lanes sharing one head sum
-  static_assert(D % E == 0 && kThreads % LG == 0, "head size must split into 16-byte lanes");
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int U = GMAX >= 8 ? 2 : kUnroll;  // tokens per batch per lane group
+  static_assert(D % E == 0 && kThreads % LG == 0 && LG <= 16 && kUnroll % 2 == 0,
+                "head size must split into at most 16 lanes of 16 bytes");
+  // Merge buffer: per (sub-row, kv head) slice GMAX*D partial sums + GMAX m and l.
+  constexpr int SLICE = GMAX * D + 2 * GMAX;
 
-  __shared__ float s_S[kHsMax * (kDecChunk + 1)];
-  __shared__ int s_blk[kDecChunk + 2];
-  __shared__ int s_bad;
+  __shared__ float s_red[(NG / 2) * SLICE];
+  __shared__ int s_blk[kBtWin];
+  __shared__ int s_tmp[8];
+  __shared__ int s_first, s_first_cum, s_bad;
 
-  const int chunk = blockIdx.x;
-  const int b = blockIdx.y / p.nslab;
-  const int slab = blockIdx.y % p.nslab;
-  const int L = p.seq_lens[b];
-  if (L < 1 || L > p.max_seq_len) return;          // combine writes NaN for b
-  const int c0 = chunk * kDecChunk;
-  if (c0 >= L) return;
-  const int nvalid = min(kDecChunk, L - c0);
-
+  const int wg = blockIdx.x;         // token range index
+  const int slab = blockIdx.y;
   const int tid = threadIdx.x;
+
+  // ---- total tokens (invalid lengths count as 0), the range, its first sequence
+  int total = 0;
+  for (int base = 0; base < p.batch; base += kThreads) {
+    const int b = base + tid;
+    const int len = b < p.batch ? valid_len(p, b) : 0;
+    const int incl = block_scan(len, s_tmp);
+    if (wg == 0 && slab == 0 && b < p.batch) p.ws_cum[b] = total + incl - len;
+    if (tid == kThreads - 1) s_tmp[5] = incl;
+    __syncthreads();
+    total += s_tmp[5];
+    __syncthreads();
+  }
+  const int per = max(p.min_tokens_per_range, (total + p.n_ranges - 1) / p.n_ranges);
+  if (wg == 0 && slab == 0 && tid == 0) {
+    p.ws_cum[p.batch] = total;       // the combine pass reads these two
+    p.ws_cum[p.batch + 1] = per;
+  }
+  const int64_t r_begin = (int64_t)wg * per;
+  if (r_begin >= total) return;
+  const int64_t r_end = min<int64_t>(r_begin + per, total);
+  {
+    int run = 0;
+    for (int base = 0; base < p.batch; base += kThreads) {
+      const int b = base + tid;
+      const int len = b < p.batch ? valid_len(p, b) : 0;
+      const int incl = run + block_scan(len, s_tmp);
+      // the one sequence with cum_excl <= r_begin < cum_incl
+      if (b < p.batch && len > 0 && incl > r_begin && incl - len <= r_begin) {
+        s_first = b;
+        s_first_cum = incl - len;
+      }
+      if (tid == kThreads - 1) s_tmp[5] = incl;
+      __syncthreads();
+      run = s_tmp[5];
+      __syncthreads();
+    }
+  }
+
   const int G = p.group;
   const int kvs = p.kvs;
-  const int R = NG / kvs;            // tokens per pass over the workgroup
+  const int R = NG / kvs;            // token streams per kv head
   const int g = tid / LG, li = tid % LG;
   const int kvl = g % kvs, r = g / kvs;
   const int kvh = slab * kvs + kvl;
   const int HS = kvs * G;
-  const int64_t row_stride = (int64_t)p.n_kv_heads * D;
+  const uint32_t row_bytes = (uint32_t)(p.n_kv_heads * D * ESZ);
   const int shift = p.block_shift;
+  const int bs_mask = (1 << shift) - 1;
+  const float c = p.scale_log2;
+  const char* kbase0 = (const char*)p.k + ((int64_t)kvh * D + li * E) * ESZ;
+  const char* vbase0 = (const char*)p.v + ((int64_t)kvh * D + li * E) * ESZ;
 
-  // Block ids of the chunk, checked against the pool once.
-  RowAddr<PAGED> addr;
-  if constexpr (PAGED) {
-    addr.blk0 = c0 >> shift;
-    const int nblk = ((c0 + nvalid - 1) >> shift) - addr.blk0 + 1;
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    for (int i = tid; i < nblk; i += kThreads) {
-      const int id = p.block_table[(int64_t)b * p.max_blocks_per_seq + addr.blk0 + i];
-      s_blk[i] = id;
-      if (id < 0 || id >= p.num_blocks) s_bad = 1;
-    }
-    addr.s_blk = s_blk;
-    addr.seq_base = 0;
-    __syncthreads();
-    if (s_bad) {
-      // A block outside the pool: poison this chunk's partial, read nothing.
-      const int64_t wbase = ((int64_t)(b * p.nslab + slab) * p.max_chunks + chunk) * HS;
-      if (tid < HS) {
-        p.ws_ml[(wbase + tid) * 2 + 0] = 0.0f;
-        p.ws_ml[(wbase + tid) * 2 + 1] = __builtin_nanf("");
+  int b = s_first;
+  int64_t cum = s_first_cum;
+  for (; b < p.batch && cum < r_end; ++b) {
+    const int L = valid_len(p, b);
+    if (L == 0) continue;
+    const int t_lo = (int)(max<int64_t>(r_begin, cum) - cum);
+    const int t_hi = (int)(min<int64_t>(r_end, cum + L) - cum);
+    cum += L;
+    if (t_hi <= t_lo) continue;
+
+    // This lane's slice of its group's G query rows.
+    uint4 q[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < G) {
+        const int64_t qoff = ((int64_t)b * p.n_heads + (int64_t)kvh * G + h) * D + li * E;
+        q[h] = *(const uint4*)((const char*)p.q + qoff * ESZ);
+      } else {
+        q[h] = make_uint4(0, 0, 0, 0);
       }
-      return;
     }
-  } else {
-    addr.s_blk = nullptr;
-    addr.blk0 = 0;
-    addr.seq_base = (int64_t)b * p.kv_capacity * row_stride;
-  }
-
-  const char* kbase = (const char*)p.k + ((int64_t)kvh * D + li * E) * (BF16 ? 2 : 4);
-  const char* vbase = (const char*)p.v + ((int64_t)kvh * D + li * E) * (BF16 ? 2 : 4);
-  constexpr int ESZ = BF16 ? 2 : 4;
-
-  // This lane's slice of its group's G query rows.
-  uint4 q[GMAX];
+    float acc[GMAX][E];
+    float m[GMAX], l[GMAX];
 #pragma unroll
-  for (int h = 0; h < GMAX; ++h) {
-    if (h < G) {
-      const int64_t qoff = ((int64_t)b * p.n_heads + (int64_t)kvh * G + h) * D + li * E;
-      q[h] = *(const uint4*)((const char*)p.q + qoff * ESZ);
-    } else {
-      q[h] = make_uint4(0, 0, 0, 0);
+    for (int h = 0; h < GMAX; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
     }
-  }
+    bool bad = false;
+    const int seq_row0 = PAGED ? 0 : b * p.kv_capacity;   // first cache row of sequence b
 
-  // ---- pass 1: raw scores q . k for every token of the chunk -> s_S[head][t]
-  const int step = R * kUnroll;
-  for (int base = 0; base < nvalid; base += step) {
-    uint4 kb[kUnroll];
+    // Sub-pieces keep the block ids they touch inside the LDS window.
+    const int span = (int)min<int64_t>(
+        PAGED ? ((int64_t)(kBtWin - 1) << shift) : (int64_t)(t_hi - t_lo), t_hi - t_lo);
+    for (int c0 = t_lo; c0 < t_hi; c0 += span) {
+      const int c1 = min(t_hi, c0 + span);
+      int blk0 = 0;
+      if constexpr (PAGED) {
+        blk0 = c0 >> shift;
+        const int nblk = ((c1 - 1) >> shift) - blk0 + 1;
+        __syncthreads();   // previous sub-piece's readers are done with s_blk
+        if (tid == 0) s_bad = 0;
+        __syncthreads();
+        for (int i = tid; i < nblk; i += kThreads) {
+          const int id = p.block_table[(int64_t)b * p.max_blocks_per_seq + blk0 + i];
+          s_blk[i] = id;
+          if (id < 0 || id >= p.num_blocks) s_bad = 1;
+        }
+        __syncthreads();
+        if (s_bad) { bad = true; break; }  // a block outside the pool: read nothing
+      }
+
+      // Load the K and V rows of the batch starting at token t0 into kx, vx.
+      auto load_batch = [&](uint4 (&kx)[U], uint4 (&vx)[U], int t0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * R + r;
-      kb[u] = make_uint4(0, 0, 0, 0);
-      if (tl < nvalid) kb[u] = *(const uint4*)(kbase + addr(c0 + tl, shift, row_stride) * ESZ);
+        for (int u = 0; u < U; ++u) {
+          const int t = t0 + u * R;
+          kx[u] = make_uint4(0, 0, 0, 0);
+          vx[u] = make_uint4(0, 0, 0, 0);
+          if (t < c1) {
+            // pool (or cache) row index; the host checks that it fits in 31 bits
+            const uint32_t row = PAGED ? (uint32_t)((s_blk[(t >> shift) - blk0] << shift) + (t & bs_mask))
+                                       : (uint32_t)(seq_row0 + t);
+            const uint64_t off = (uint64_t)row * row_bytes;
+            kx[u] = *(const uint4*)(kbase0 + off);
+            vx[u] = *(const uint4*)(vbase0 + off);
+          }
+        }
+      };
+      // Scores, online softmax and p * v for the batch at t0.
+      auto consume = [&](const uint4 (&kx)[U], const uint4 (&vx)[U], int t0) {
+        float s[U][GMAX];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          dot_rows<BF16, GMAX>(q, kx[u], s[u]);
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h) s[u][h] = group_sum<LG>(s[u][h]);
+        }
+        // Online softmax against a reference max m: rescale only when a score
+        // exceeds m by more than 2^kLazy in the exp2 domain (weights stay <= 2^kLazy).
+        bool grow = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h)
+            if (t0 + u * R < c1) grow |= (s[u][h] - m[h]) * c > kLazy;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform branch
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h) {
+            float mb = s[0][h];
+#pragma unroll
+            for (int u = 1; u < U; ++u)
+              if (t0 + u * R < c1) mb = fmaxf(mb, s[u][h]);
+            const float m_new = fmaxf(m[h], mb);
+            const float alpha = m[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m[h] - m_new) * c);
+            m[h] = m_new;
+            l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h) {   // the weights overwrite the scores
+            s[u][h] = t0 + u * R < c1 ? __builtin_amdgcn_exp2f((s[u][h] - m[h]) * c) : 0.0f;
+            l[h] += s[u][h];
+          }
+        if constexpr (BF16) {
+          // p * v over token pairs on v_dot2_f32_bf16: (p_u, p_u+1) . (v_u[e], v_u+1[e])
+#pragma unroll
+          for (int u = 0; u < U; u += 2) {
+            uint32_t vp[E];
+            const uint32_t a[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+            const uint32_t bb[4] = {vx[u + 1].x, vx[u + 1].y, vx[u + 1].z, vx[u + 1].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              vp[2 * i] = __builtin_amdgcn_perm(bb[i], a[i], 0x05040100u);      // low halves
+              vp[2 * i + 1] = __builtin_amdgcn_perm(bb[i], a[i], 0x07060302u);  // high halves
+            }
+#pragma unroll
+            for (int h = 0; h < GMAX; ++h) {
+              const uint32_t pp = pack_bf16x2(s[u][h], s[u + 1][h]);
+#pragma unroll
+              for (int e = 0; e < E; ++e) acc[h][e] = dot2_bf16(pp, vp[e], acc[h][e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float x[E];
+            unpack16<BF16>(vx[u], x);
+#pragma unroll
+            for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+              for (int e = 0; e < E; ++e) acc[h][e] = fmaf(s[u][h], x[e], acc[h][e]);
+          }
+        }
+      };
+      for (int t0 = c0 + r; t0 < c1; t0 += R * U) {
+        uint4 kx[U], vx[U];
+        load_batch(kx, vx, t0);
+        consume(kx, vx, t0);
+      }
     }
+
+    const int64_t slot = (int64_t)(wg + b) * p.n_heads + (int64_t)slab * HS;
+    if (bad) {
+      if (tid < HS) {
+        p.ws_ml[(slot + tid) * 2 + 0] = 0.0f;
+        p.ws_ml[(slot + tid) * 2 + 1] = __builtin_nanf("");
+      }
+      __syncthreads();
+      continue;
+    }
+    // ---- fixed-order tree over the token streams: state(r) (+)= state(r + s)
+    for (int s2 = R / 2; s2 >= 1; s2 /= 2) {
+      __syncthreads();
+      if (r >= s2 && r < 2 * s2) {
+        float* dst = s_red + ((r - s2) * kvs + kvl) * SLICE;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * R + r;
-      float s[GMAX];
-      dot_rows<BF16, GMAX>(q, kb[u], s);
-      reduce_scatter<LG, GMAX>(s, li);
-      if (tl < nvalid && (li % LPH) == 0) {
+        for (int h = 0; h < GMAX; ++h) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int h = (li / LPH) * NV + i;
-          if (h < G) s_S[(kvl * G + h) * (kDecChunk + 1) + tl] = s[i];
+          for (int e = 0; e < E; ++e) dst[(h * E + e) * LG + li] = acc[h][e];
+          if (li == 0) {
+            dst[GMAX * D + h] = m[h];
+            dst[GMAX * D + GMAX + h] = l[h];
+          }
+        }
+      }
+      __syncthreads();
+      if (r < s2) {
+        const float* src = s_red + (r * kvs + kvl) * SLICE;
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          const float mo = src[GMAX * D + h];
+          const float M = fmaxf(m[h], mo);
+          const float a = m[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m[h] - M) * c);
+          const float bo = mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mo - M) * c);
+          m[h] = M;
+          l[h] = l[h] * a + src[GMAX * D + GMAX + h] * bo;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[h][e] = acc[h][e] * a + src[(h * E + e) * LG + li] * bo;
         }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- pass 2: per-head softmax over the chunk (log2 domain)
-  const int wave = tid / 64, lane = tid % 64;
-  const float c = p.scale_log2;
-  const int64_t wbase = ((int64_t)(b * p.nslab + slab) * p.max_chunks + chunk) * HS;
-  for (int hs = wave; hs < HS; hs += kThreads / 64) {
-    float* row = s_S + hs * (kDecChunk + 1);
-    float x[kDecChunk / 64];
-    float m = -INFINITY;
+    if (r == 0) {
 #pragma unroll
-    for (int j = 0; j < kDecChunk / 64; ++j) {
-      const int t = lane + 64 * j;
-      x[j] = t < nvalid ? row[t] : -INFINITY;
-      m = fmaxf(m, x[j]);
-    }
-    m = wave_max(m);
-    float sum = 0.0f;
+      for (int h = 0; h < GMAX; ++h) {
+        if (h < G) {
+          float* d = p.ws_o + (slot + kvl * G + h) * D + li * E;
 #pragma unroll
-    for (int j = 0; j < kDecChunk / 64; ++j) {
-      const int t = lane + 64 * j;
-      const float e = t < nvalid ? __builtin_amdgcn_exp2f((x[j] - m) * c) : 0.0f;
-      row[t] = e;
-      sum += e;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      p.ws_ml[(wbase + hs) * 2 + 0] = m * c;
-      p.ws_ml[(wbase + hs) * 2 + 1] = sum;
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 3: O += p * v over this lane's token sub-row
-  float acc[GMAX][E];
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
-
-  for (int base = 0; base < nvalid; base += step) {
-    uint4 vb[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * R + r;
-      vb[u] = make_uint4(0, 0, 0, 0);
-      if (tl < nvalid) vb[u] = *(const uint4*)(vbase + addr(c0 + tl, shift, row_stride) * ESZ);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * R + r;
-      if (tl < nvalid) {
-        float x[E];
-        unpack16<BF16>(vb[u], x);
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h) {
-          if (h < G) {
-            const float pw = s_S[(kvl * G + h) * (kDecChunk + 1) + tl];
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pw, x[e], acc[h][e]);
+          for (int e = 0; e < E; e += 4)
+            *(float4*)(d + e) = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+          if (li == 0) {
+            p.ws_ml[(slot + kvl * G + h) * 2 + 0] = m[h] * c;
+            p.ws_ml[(slot + kvl * G + h) * 2 + 1] = l[h];
           }
         }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- fixed-order tree over the token sub-rows: acc(r) += acc(r + s)
-  float* red = s_S;  // reused: (NG / 2) * GMAX * D floats <= kHsMax * (kDecChunk + 1)
-  constexpr int SLICE = GMAX * E * LG;  // floats per (sub-row, kv head)
-  static_assert((NG / 2) * GMAX * D <= kHsMax * (kDecChunk + 1), "reduction buffer too small");
-  for (int s = R / 2; s >= 1; s /= 2) {
-    if (r >= s && r < 2 * s) {
-      float* dst = red + ((r - s) * kvs + kvl) * SLICE;
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e) dst[(h * E + e) * LG + li] = acc[h][e];
-    }
     __syncthreads();
-    if (r < s) {
-      const float* src = red + (r * kvs + kvl) * SLICE;
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] += src[(h * E + e) * LG + li];
-    }
-    __syncthreads();
-  }
-
-  if (r == 0) {
-    float* dst = p.ws_o + wbase * D;
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      if (h < G) {
-        float* d = dst + (int64_t)(kvl * G + h) * D + li * E;
-#pragma unroll
-        for (int e = 0; e < E; e += 4)
-          *(float4*)(d + e) = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
-      }
-    }
   }
 }
 
-// Merge the chunk partials of one (sequence, slab) in chunk order:
-//   o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c.
+// Merge the pieces of one sequence in range order, one thread per output:
+//   o = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w,
+// computed in one pass with a running maximum (four pieces per step so their
+// loads overlap).
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
-  const int b = blockIdx.x / p.nslab;
-  const int slab = blockIdx.x % p.nslab;
-  const int HS = p.kvs * p.group;
+  constexpr int HPW = kThreads / D > 0 ? kThreads / D : 1;  // heads per workgroup
+  const int hgroups = (p.n_heads + HPW - 1) / HPW;
+  const int b = blockIdx.x / hgroups;
+  const int h = (blockIdx.x % hgroups) * HPW + threadIdx.x / D;
+  const int d = threadIdx.x % D;
+  if (h >= p.n_heads) return;
   const int L = p.seq_lens[b];
-  const bool bad = L < 1 || L > p.max_seq_len;
-  const int nch = bad ? 0 : (L + kDecChunk - 1) / kDecChunk;
-  const int64_t wbase = (int64_t)(b * p.nslab + slab) * p.max_chunks * HS;
-  for (int idx = threadIdx.x; idx < HS * D; idx += kThreads) {
-    const int hs = idx / D, d = idx % D;
-    float out;
-    if (bad) {
-      out = __builtin_nanf("");
-    } else {
-      float M = -INFINITY;
-      for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, p.ws_ml[(wbase + ch * HS + hs) * 2]);
-      float num = 0.0f, den = 0.0f;
-      for (int ch = 0; ch < nch; ++ch) {
-        const int64_t w = wbase + ch * HS + hs;
-        const float wt = __builtin_amdgcn_exp2f(p.ws_ml[w * 2] - M);
-        num = fmaf(wt, p.ws_o[w * D + d], num);
-        den = fmaf(wt, p.ws_ml[w * 2 + 1], den);
+  float out = __builtin_nanf("");
+  if (L >= 1 && L <= p.max_seq_len) {
+    const int per = p.ws_cum[p.batch + 1];
+    const int cb = p.ws_cum[b];
+    const int w0 = cb / per, w1 = (cb + L - 1) / per;
+    float M = -INFINITY, num = 0.0f, den = 0.0f;
+    for (int w = w0; w <= w1; w += 4) {
+      float mm[4], ll[4], oo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t s = (int64_t)(w + j + b) * p.n_heads + h;
+        const bool ok = w + j <= w1;
+        mm[j] = ok ? p.ws_ml[s * 2] : -INFINITY;
+        ll[j] = ok ? p.ws_ml[s * 2 + 1] : 0.0f;
+        oo[j] = ok ? p.ws_o[s * D + d] : 0.0f;
       }
-      out = num / den;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (w + j <= w1) {
+          const float Mn = fmaxf(M, mm[j]);
+          const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+          const float wt = __builtin_amdgcn_exp2f(mm[j] - Mn);
+          num = fmaf(wt, oo[j], num * a);
+          den = fmaf(wt, ll[j], den * a);
+          M = Mn;
+        }
+      }
     }
-    const int h = slab * HS + hs;
-    const int64_t o = ((int64_t)b * p.n_heads + h) * D + d;
-    if constexpr (BF16) {
-      ((__bf16*)p.o)[o] = (__bf16)out;
-    } else {
-      ((float*)p.o)[o] = out;
-    }
+    out = num / den;
   }
+  const int64_t o = ((int64_t)b * p.n_heads + h) * D + d;
+  if constexpr (BF16) {
+    ((__bf16*)p.o)[o] = (__bf16)out;
+  } else {
+    ((float*)p.o)[o] = out;
+  }
+}
+
+// Token ranges for one launch: one per workgroup slot the device can keep
+// resident (compute units x workgroups per unit), never more than the
+// workspace holds or than min-size ranges the batch can fill. The slot count
+// is the smaller of the contiguous and paged kernels' occupancy, so the two
+// entry points always cut the same ranges and stay bitwise equal.
+template <bool BF16, int D, int GMAX>
+int resident_ranges(const DecodeParams& p) {
+  int dev = 0, cus = 0, occ_c = 0, occ_p = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_c, decode_partial<BF16, D, GMAX, false>,
+                                                   kThreads, 0) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, decode_partial<BF16, D, GMAX, true>,
+                                                   kThreads, 0) != hipSuccess) return -1;
+  const int slots = cus * max(1, min(occ_c, occ_p)) / p.nslab;
+  return max(1, min(p.n_ranges, slots));
 }
 
 template <bool BF16, int D, int GMAX, bool PAGED>
-int launch_one(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.max_chunks, p.batch * p.nslab);
+int launch_one(DecodeParams p, hipStream_t stream) {
+  p.n_ranges = resident_ranges<BF16, D, GMAX>(p);
+  if (p.n_ranges < 1) return kEhip;
+  dim3 grid(p.n_ranges, p.nslab);
   hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED>), grid, dim3(kThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return kEhip;
-  hipLaunchKernelGGL((decode_combine<BF16, D>), dim3(p.batch * p.nslab), dim3(kThreads), 0,
-                     stream, p);
+  constexpr int HPW = kThreads / D > 0 ? kThreads / D : 1;
+  const int cgrid = p.batch * ((p.n_heads + HPW - 1) / HPW);
+  hipLaunchKernelGGL((decode_combine<BF16, D>), dim3(cgrid), dim3(kThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return kEhip;
   return kOk;
 }
@@ -358,7 +480,8 @@ int launch_g(const DecodeParams& p, int gmax, hipStream_t stream) {
 
 }  // namespace
 
-int decode_chunk_tokens() { return kDecChunk; }
+int decode_max_ranges() { return 2048; }          // 256 CUs x 8 resident workgroups
+int decode_min_tokens_per_range() { return 64; }
 int decode_heads_per_slab_max() { return kHsMax; }
 
 bool decode_supported(bool bf16, int head_dim) {

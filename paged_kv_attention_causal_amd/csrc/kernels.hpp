@@ -20,19 +20,22 @@ struct DecodeParams {
   void* o;                    // [batch, n_heads, D]
   const int32_t* seq_lens;    // [batch]
   const int32_t* block_table; // [batch, max_blocks_per_seq] (paged)
-  float* ws_o;                // [batch, nslab, max_chunks, HS, D] partial outputs
-  float* ws_ml;               // [batch, nslab, max_chunks, HS, 2] (m * scale * log2e, l)
+  float* ws_o;                // [n_ranges + batch, n_heads, D] partial outputs, slot = range + seq
+  float* ws_ml;               // [n_ranges + batch, n_heads, 2] (m * scale * log2e, l)
+  int* ws_cum;                // [batch + 2]: exclusive prefix of lengths, total, tokens per range
   int batch, n_heads, n_kv_heads, group;
   int kvs;                    // KV heads per workgroup slab
   int nslab;                  // n_kv_heads / kvs
-  int max_chunks;
+  int n_ranges;               // equal token ranges the sequences are cut into
+  int min_tokens_per_range;
   int max_seq_len;
   int max_blocks_per_seq, block_shift, num_blocks;
   int kv_capacity;
   float scale_log2;           // attention_scale * log2(e)
 };
 
-int decode_chunk_tokens();
+int decode_max_ranges();
+int decode_min_tokens_per_range();
 int decode_heads_per_slab_max();
 bool decode_supported(bool bf16, int head_dim);
 int decode_lanes_per_row(bool bf16, int head_dim);

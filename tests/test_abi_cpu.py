@@ -116,9 +116,14 @@ def test_contig_decode_capacity_validation(L):
 
 
 def test_decode_workspace_size_formula(L):
-    # chunks of 256 tokens; per (sequence, chunk, head): head_dim + 2 floats
-    assert L.attn_decode_workspace_size(64, 32, 8, 128, 8192) == 64 * 32 * 32 * 130 * 4
-    assert L.attn_decode_workspace_size(1, 4, 2, 16, 72) == 1 * 1 * 4 * 18 * 4
+    # slots = ranges + batch, ranges <= min(2048, ceil(batch * max_seq_len / 64));
+    # per slot and head: head_dim + 2 floats; then batch + 2 int32 prefix sums
+    def expect(B, H, D, maxlen):
+        ranges = min(2048, -(-B * maxlen // 64))
+        return (ranges + B) * H * (D + 2) * 4 + (B + 2) * 4
+    assert L.attn_decode_workspace_size(64, 32, 8, 128, 8192) == expect(64, 32, 128, 8192)
+    assert expect(64, 32, 128, 8192) == 2112 * 32 * 130 * 4 + 66 * 4
+    assert L.attn_decode_workspace_size(1, 4, 2, 16, 72) == expect(1, 4, 16, 72) == 3 * 4 * 18 * 4 + 12
     assert L.attn_decode_workspace_size(1, 4, 3, 16, 72) == 0     # invalid heads
     assert L.attn_decode_workspace_size(0, 4, 2, 16, 72) == 0
 

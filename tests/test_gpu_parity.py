@@ -296,8 +296,13 @@ def test_decode_bad_entries_give_nan_only_there():
     bt[3, 1] = -5
     o = host(_run_paged(c, bt=i32(bt), lens=i32(lens)))
     assert np.all(np.isnan(o[1])) and np.all(np.isnan(o[3]))
-    for b in (0, 2, 4):
-        assert np.array_equal(o[b], clean[b])
+    # The other sequences stay correct. (The token ranges are cut over the valid
+    # lengths, so their rounding may differ from the clean run's.)
+    keep = [0, 2, 4]
+    ref = O.decode_paged(c.q, c.k_pool, c.v_pool, c.block_table, 16, c.seq_lens, 8, 2, c.scale,
+                         batch_indices=keep)
+    check(o[keep], ref, "bf16", "untouched sequences")
+    check(clean[keep], ref, "bf16", "clean run")
 
 
 # ------------------------------------------------------------------ MLA
