@@ -6,14 +6,15 @@
 // loaded once per workgroup and serves all of its heads.
 //
 // One workgroup = 4 waves = 16 heads of one sequence over a token range.
-// Per 64-token tile:
-//   the tile is staged in LDS twice: row-major [64 x (R+P)] for the scores
-//   and transposed [R x 64] for the value product;
+// 64-token latent tiles move through a two-stage LDS ring (row-major, padded
+// rows): the next tile is loaded into registers while the current one is
+// consumed. Per tile:
 //   wave w computes S^T = L Q^T for tokens 16w..16w+15 (16x16x32 bf16 MFMA,
 //   Q^T in registers) and writes the raw scores to LDS;
 //   every wave then reads all 64 scores of its lane's head, runs the same
 //   online-softmax update (identical in all four waves), and accumulates its
-//   own quarter of the value width: O^T[128w .. 128w+127] += V^T P^T.
+//   own quarter of the value width, O^T[128w .. 128w+127] += V^T P^T, with
+//   the V^T operand read from the row-major tile by ds_read_b64_tr_b16.
 // When the batch already fills the chip each workgroup takes a whole
 // sequence and writes o_lat directly; otherwise the context is split and
 // mla_combine merges the pieces in split order.
@@ -31,7 +32,6 @@ constexpr int kR = 512;          // kv_lora_rank
 constexpr int kP = 64;           // qk_rope_head_dim
 constexpr int kW = kR + kP;      // latent row width
 constexpr int kLatStr = kW + 8;  // padded row stride of the row-major tile
-constexpr int kVtStr = kTile + 8;
 constexpr int kSStr = kTile + 4;
 constexpr int kKSteps = kW / 32; // MFMA k-steps for the scores (18)
 constexpr int kDPerWave = kR / 4;
@@ -49,9 +49,21 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
   return (i % kXcd) * (n / kXcd) + i / kXcd;
 }
 
+// Transposed LDS read: four consecutive rows of one 16-bit column per lane.
+__device__ __forceinline__ bf16x4_t ds_read_tr16(const void* p) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4_t, v);
+}
+
 __global__ __launch_bounds__(kThreads) void mla_kernel(MlaParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 sLat[kTile * kLatStr];
-  __shared__ __attribute__((aligned(16))) __bf16 sVt[kR * kVtStr];
+  constexpr int kRowB = kLatStr * 2;                    // padded row bytes in LDS
+  constexpr int kChunks = kTile * (kW / 8);             // 16-byte chunks per tile
+  constexpr int kLpt = kChunks / kThreads;              // loads per thread per tile
+  static_assert(kChunks % kThreads == 0, "tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) __bf16 sLat[2][kTile * kLatStr];
   __shared__ __attribute__((aligned(16))) float sS[kHeads * kSStr];
 
   const int n_hg = p.n_heads / kHeads;
@@ -85,38 +97,46 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(MlaParams p) {
   float m_run = -INFINITY;
   float l_run = 0.0f;
   const float c = p.scale_log2;
-  const __bf16* lat = (const __bf16*)p.latent + (int64_t)b * p.kv_capacity * kW;
+  const char* lat = (const char*)p.latent + (int64_t)b * p.kv_capacity * (kW * 2);
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    __syncthreads();
-    // ---- stage the tile: row-major for the scores, transposed for the value
-    for (int u = tid; u < (kTile / 4) * (kW / 8); u += kThreads) {
-      const int tq = u / (kW / 8), seg = u % (kW / 8);
-      bf16x8_t x[4];
+  // Tile fetch into registers (tokens past t_end read as zero) and stash to LDS.
+  uint4 st[kLpt];
+  auto fetch = [&](int t0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + 4 * tq + j;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (t < t_end) w = *(const uint4*)(lat + (int64_t)t * kW + seg * 8);
-        x[j] = __builtin_bit_cast(bf16x8_t, w);
-        *(bf16x8_t*)(sLat + (4 * tq + j) * kLatStr + seg * 8) = x[j];
-      }
-      if (seg < kR / 8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bf16x4_t v4 = {x[0][e], x[1][e], x[2][e], x[3][e]};
-          *(bf16x4_t*)(sVt + (seg * 8 + e) * kVtStr + 4 * tq) = v4;
-        }
-      }
+    for (int j = 0; j < kLpt; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / (kW / 8), cc = ci % (kW / 8);
+      const int t = t0 + row;
+      st[j] = make_uint4(0, 0, 0, 0);
+      if (t < t_end) st[j] = *(const uint4*)(lat + (int64_t)t * (kW * 2) + cc * 16);
     }
+  };
+  auto stash = [&](int stage) {
+#pragma unroll
+    for (int j = 0; j < kLpt; ++j) {
+      const int ci = tid + kThreads * j;
+      const int row = ci / (kW / 8), cc = ci % (kW / 8);
+      *(uint4*)((char*)sLat[stage] + row * kRowB + cc * 16) = st[j];
+    }
+  };
+
+  if (t_begin < t_end) {
+    fetch(t_begin);
+    stash(0);
     __syncthreads();
+  }
+  int stage = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += kTile, stage ^= 1) {
+    const bool more = t0 + kTile < t_end;
+    if (more) fetch(t0 + kTile);
+    const char* tile = (const char*)sLat[stage];
 
     // ---- raw scores for tokens 16*wave .. +15 of the tile
     {
       f32x4_t acc = f32x4_t{};
-      const __bf16* lrow = sLat + (16 * wave + l16) * kLatStr + 8 * quad;
+      const char* lrow = tile + (16 * wave + l16) * kRowB + 16 * quad;
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) acc = mma16(*(const bf16x8_t*)(lrow + 32 * kk), qB[kk], acc);
+      for (int kk = 0; kk < kKSteps; ++kk) acc = mma16(*(const bf16x8_t*)(lrow + 64 * kk), qB[kk], acc);
       // accumulator: lane l16 = head, rows = tokens 16*wave + 4*quad + r
       *(f32x4_t*)(sS + l16 * kSStr + 16 * wave + 4 * quad) = acc;
     }
@@ -163,14 +183,23 @@ __global__ __launch_bounds__(kThreads) void mla_kernel(MlaParams p) {
 #pragma unroll
     for (int db = 0; db < kDPerWave / 16; ++db) oacc[db] *= alpha;
 
-    // ---- O^T[this wave's quarter] += V^T P^T (tokens 32*pp + 8*quad + j)
+    // ---- O^T[this wave's quarter] += V^T P^T over tokens 32*pp + 8*quad + j.
+    // Lane (quad, l16) addresses row k0 + l16/4 at columns 4*(l16%4)..+3 of a
+    // 16-column slice and receives column (slice + l16) of rows k0 .. k0+3.
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+    for (int pp = 0; pp < 2; ++pp) {
+      const int r0 = 32 * pp + 8 * quad + l16 / 4;
 #pragma unroll
       for (int db = 0; db < kDPerWave / 16; ++db) {
-        const __bf16* vrow = sVt + (kDPerWave * wave + 16 * db + l16) * kVtStr + 32 * pp + 8 * quad;
-        oacc[db] = mma16(*(const bf16x8_t*)vrow, pB[pp], oacc[db]);
+        const int col = kDPerWave * wave + 16 * db + 4 * (l16 % 4);
+        const bf16x4_t lo = ds_read_tr16(tile + r0 * kRowB + col * 2);
+        const bf16x4_t hi = ds_read_tr16(tile + (r0 + 4) * kRowB + col * 2);
+        const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[db] = mma16(a, pB[pp], oacc[db]);
       }
+    }
+    if (more) stash(stage ^ 1);
+    __syncthreads();
   }
 
   // ---- epilogue: the head's sum is spread over the 4 lanes l16 + 16*quad
