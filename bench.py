@@ -72,8 +72,10 @@ def parse():
                     help="skip timing the f64 oracle on the host")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle sample")
-    ap.add_argument("--only", choices=["decode", "mla", "chunked", "prefill"], default=None,
-                    help="time one workload only (for profiler runs)")
+    ap.add_argument("--only", choices=["decode", "mla", "chunked", "prefill", "copy"], default=None,
+                    help="time one workload only (for profiler runs); 'copy' runs a plain 1 GiB "
+                         "device copy three times, the calibration for the FETCH_SIZE / "
+                         "WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -96,6 +98,14 @@ def main():
     pk.lib()  # fail loudly here if the HIP library is missing
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        x = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)   # exactly 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": x.numel() * 2, "launches": 3}))
+        return
 
     def to(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
