@@ -9,8 +9,8 @@
 // wave owns 32 rows. Key tiles of 64 rows move through a two-stage LDS ring:
 // while a tile is consumed, the next one is loaded into registers and
 // written to the other stage afterwards, so there is one barrier per tile.
-// K and V stay row-major in LDS with their 16-byte chunks XOR-swizzled by
-// row, which keeps both operand reads free of bank conflicts:
+// K and V stay row-major in LDS with padded rows, which keeps the operand
+// reads free of bank conflicts and their addresses immediate offsets:
 //   S^T = K Q^T on 32x32 MFMAs (Q^T in registers as the B operand): in the
 //     accumulator layout lane l owns query row l % 32 and 16 of each 32 keys,
 //     the other 16 sit in lane l ^ 32; the row max needs one cross-half
@@ -35,7 +35,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;    // keys per tile
-constexpr int kBtWin = 1024;   // block-table entries cached in LDS
+constexpr int kBtWin = 256;    // block-table entries cached in LDS
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 
 template <bool BF16>
@@ -80,7 +80,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   constexpr int E = 16 / ESZ;                 // elements per 16-byte chunk
   constexpr int ROWB = D * ESZ;               // bytes per K/V row
   constexpr int CPR = ROWB / 16;              // chunks per row
-  constexpr int TILEB = kBlockN * ROWB;       // bytes per K (or V) tile
+  // LDS row stride: 256-byte bf16 rows padded to 304 bytes (76 words, 12 banks
+  // apart): the 16 rows of a K-operand read start in 16 different bank
+  // groups and the 4 rows of a transposed V read cover disjoint banks, with
+  // every LDS address a lane base plus an immediate.
+  constexpr int LROW = BF16 ? ROWB + 48 : ROWB + 16;
+  constexpr int TILEB = kBlockN * LROW;       // LDS bytes per K (or V) tile
   constexpr int NCH = kBlockN * CPR;          // chunks per tile
   constexpr int LPT = (NCH + kThreads - 1) / kThreads;  // chunk loads per thread per tile
   constexpr int DB = (D + 31) / 32;           // 32-row blocks of O^T
@@ -120,10 +125,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int seq_row0 = PAGED ? 0 : b * p.kv_capacity;
   int win0 = 0, win_end = 0;   // block-table window [win0, win_end) held in s_bt
   if (tid == 0) s_bad = 0;
-
-  // Chunk c of row r lives at chunk (c ^ swz(r)), which spreads the rows of
-  // one operand read over different banks.
-  auto swz = [](int r) { return CPR >= 16 ? 2 * (r & 7) : 0; };
 
   // (Re)load the block-table window so it starts at block blk; validates ids.
   auto load_window = [&](int blk) {
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const int ci = tid + kThreads * j;
       if (ci < NCH) {
         const int row = ci / CPR, cc = ci % CPR;
-        const int o = row * ROWB + ((cc ^ swz(row)) * 16);
+        const int o = row * LROW + cc * 16;
         *(uint4*)(s_kv[stage][0] + o) = stK[j];
         *(uint4*)(s_kv[stage][1] + o) = stV[j];
       }
@@ -240,9 +241,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           for (int kk = 0; kk < KSTEPS; ++kk) {
             typename M::Op a;
             if constexpr (BF16) {
-              a = *(const bf16x8_t*)(sK + row * ROWB + (((2 * kk + hf) ^ swz(row)) * 16));
+              a = *(const bf16x8_t*)(sK + row * LROW + (2 * kk + hf) * 16);
             } else {
-              a = *(const float*)(sK + row * ROWB + (kk * 2 + hf) * 4);
+              a = *(const float*)(sK + row * LROW + (kk * 2 + hf) * 4);
             }
             acc = M::mma(a, qB[kk], acc);
           }
@@ -326,10 +327,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
               for (int db = 0; db < DB; ++db) {
                 const int chunk = 4 * db + 2 * (g16 % 2) + (i16 % 4) / 2;
-                const bf16x4_t lo =
-                    ds_read_tr16(sV + lo_row * ROWB + ((chunk ^ swz(lo_row)) * 16) + 8 * (i16 % 2));
-                const bf16x4_t hi =
-                    ds_read_tr16(sV + hi_row * ROWB + ((chunk ^ swz(hi_row)) * 16) + 8 * (i16 % 2));
+                const bf16x4_t lo = ds_read_tr16(sV + lo_row * LROW + chunk * 16 + 8 * (i16 % 2));
+                const bf16x4_t hi = ds_read_tr16(sV + hi_row * LROW + chunk * 16 + 8 * (i16 % 2));
                 const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[db] = M::mma(a, pb, oacc[db]);
               }
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
               for (int db = 0; db < DB; ++db) {
                 const int d = db * 32 + lr;
-                const float a = d < D ? *(const float*)(sV + key * ROWB + d * 4) : 0.0f;
+                const float a = d < D ? *(const float*)(sV + key * LROW + d * 4) : 0.0f;
                 oacc[db] = M::mma(a, s[kb][r], oacc[db]);
               }
             }
