@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -154,7 +155,11 @@ int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o
   p.num_blocks = paged ? num_blocks : 0;
   p.kv_capacity = paged ? 0 : kv_capacity;
   p.q_tiles = (int)q_tiles;
-  p.scale_log2 = attention_scale * pkva::kLog2eHost;
+  // The kernel masks a score by making it -inf and relies on exp2(-inf * c) = 0,
+  // which needs c > 0. A zero scale makes every visible score 0 (uniform
+  // weights); the smallest normal float gives the same weights, exp2 of a
+  // product that small being exactly 1.
+  p.scale_log2 = std::max(attention_scale * pkva::kLog2eHost, FLT_MIN);
   const int rc = pkva::launch_prefill(bf16, paged, head_dim, p, (hipStream_t)stream);
   return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
 }

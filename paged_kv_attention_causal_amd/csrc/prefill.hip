@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int kvh = h / p.group;
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
   const int q0 = qt * kBlockM;
   const int off = p.position_offset;
@@ -139,28 +139,51 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     __syncthreads();
   };
 
-  // Global loads of key tile kt into registers (16-byte chunks); rows past
-  // last_key are masked for every row of the tile and read as zero.
+  // Global loads of key tile kt into registers (16-byte chunks). Rows past
+  // last_key are masked for every row of the tile and read as zero; tiles
+  // wholly below it load unconditionally from a uniform base and a
+  // loop-invariant per-thread offset.
   uint4 stK[LPT], stV[LPT];
+  static_assert(NCH % kThreads == 0, "every thread loads the same number of chunks");
   auto fetch = [&](int kt) {
     const int k0 = kt * kBlockN;
+    if (k0 + kBlockN - 1 <= last_key) {
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ci = tid + kThreads * j;
-      const int row = ci / CPR, cc = ci % CPR;
-      const int t = k0 + row;
-      stK[j] = make_uint4(0, 0, 0, 0);
-      stV[j] = make_uint4(0, 0, 0, 0);
-      if (ci < NCH && t <= last_key) {
-        uint32_t prow;
+      for (int j = 0; j < LPT; ++j) {
+        const int ci = tid + kThreads * j;
+        const int row = ci / CPR, cc = ci % CPR;
         if constexpr (PAGED) {
-          prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
+          const int t = k0 + row;
+          const uint32_t prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
+          const uint64_t o = (uint64_t)prow * row_bytes + (uint32_t)(cc * 16);
+          stK[j] = *(const uint4*)(kg + o);
+          stV[j] = *(const uint4*)(vg + o);
         } else {
-          prow = (uint32_t)(seq_row0 + t);
+          const int64_t tb = (int64_t)(seq_row0 + k0) * row_bytes;
+          const uint32_t o = (uint32_t)row * row_bytes + (uint32_t)(cc * 16);
+          stK[j] = *(const uint4*)(kg + tb + o);
+          stV[j] = *(const uint4*)(vg + tb + o);
         }
-        const uint64_t o = (uint64_t)prow * row_bytes + (uint32_t)(cc * 16);
-        stK[j] = *(const uint4*)(kg + o);
-        stV[j] = *(const uint4*)(vg + o);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int ci = tid + kThreads * j;
+        const int row = ci / CPR, cc = ci % CPR;
+        const int t = k0 + row;
+        stK[j] = make_uint4(0, 0, 0, 0);
+        stV[j] = make_uint4(0, 0, 0, 0);
+        if (t <= last_key) {
+          uint32_t prow;
+          if constexpr (PAGED) {
+            prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
+          } else {
+            prow = (uint32_t)(seq_row0 + t);
+          }
+          const uint64_t o = (uint64_t)prow * row_bytes + (uint32_t)(cc * 16);
+          stK[j] = *(const uint4*)(kg + o);
+          stV[j] = *(const uint4*)(vg + o);
+        }
       }
     }
   };
@@ -168,12 +191,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int ci = tid + kThreads * j;
-      if (ci < NCH) {
-        const int row = ci / CPR, cc = ci % CPR;
-        const int o = row * LROW + cc * 16;
-        *(uint4*)(s_kv[stage][0] + o) = stK[j];
-        *(uint4*)(s_kv[stage][1] + o) = stV[j];
-      }
+      const int row = ci / CPR, cc = ci % CPR;
+      const int o = row * LROW + cc * 16;
+      *(uint4*)(s_kv[stage][0] + o) = stK[j];
+      *(uint4*)(s_kv[stage][1] + o) = stV[j];
     }
   };
 
@@ -209,11 +230,130 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int my_pos = off + qrow;
     const bool wave_live = q0 + wave * 32 < p.seq_q;
 
+    // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+    auto tile = [&](bool need_mask, int k0, int stage) {
+      const char* sK = s_kv[stage][0];
+      const char* sV = s_kv[stage][1];
+      f32x16_t s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16_t acc = f32x16_t{};
+        const int row = kb * 32 + lr;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          typename M::Op a;
+          if constexpr (BF16) {
+            a = *(const bf16x8_t*)(sK + row * LROW + (2 * kk + hf) * 16);
+          } else {
+            a = *(const float*)(sK + row * LROW + (kk * 2 + hf) * 4);
+          }
+          acc = M::mma(a, qB[kk], acc);
+        }
+        s[kb] = acc;
+      }
+
+      // Accumulator register r of key block kb holds key k0 + 32*kb + 8*(r/4) + 4*hf + r%4.
+      if (need_mask) {
+        const int lim = min(my_pos, p.seq_kv - 1) - (k0 + 4 * hf);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r / 4) + (r % 4) > lim) s[kb][r] = -INFINITY;
+      }
+
+      // Row max over this lane's 32 keys, then across the two lane halves.
+      // (maximum, not maxnum: no canonicalising moves; scores carry no NaN
+      // unless the inputs do, and then the row is NaN either way.)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[kb][r]), s[kb][r + 1]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > kLazy) != 0) {   // wave-uniform
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha =
+            m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      // Key 0 is visible to every row, so m_ref is finite from the first tile on.
+      const float mc = m_ref == -INFINITY ? 0.0f : m_ref * c;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sv = s[kb][r];
+          const float x = BF16 ? fmaf(sv, c, -mc) : (sv - m_ref) * c;
+          s[kb][r] = __builtin_amdgcn_exp2f(x);   // masked: exp2(-inf) = 0
+        }
+
+      if constexpr (BF16) {
+        float psum = 0.0f;
+        const uint32_t ones = 0x3f803f80u;
+        const int g16 = lane / 16, i16 = lane % 16;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            bf16x8_t pb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[kb][8 * mm + j];
+            const auto w = __builtin_bit_cast(uint4, pb);
+            psum = dot2_bf16(w.x, ones, psum);
+            psum = dot2_bf16(w.y, ones, psum);
+            psum = dot2_bf16(w.z, ones, psum);
+            psum = dot2_bf16(w.w, ones, psum);
+            const int lo_row = kb * 32 + 16 * mm + 4 * hf + i16 / 4;
+            const int hi_row = lo_row + 8;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int chunk = 4 * db + 2 * (g16 % 2) + (i16 % 4) / 2;
+              const bf16x4_t lo = ds_read_tr16(sV + lo_row * LROW + chunk * 16 + 8 * (i16 % 2));
+              const bf16x4_t hi = ds_read_tr16(sV + hi_row * LROW + chunk * 16 + 8 * (i16 % 2));
+              const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              oacc[db] = M::mma(a, pb, oacc[db]);
+            }
+          }
+        }
+        l_run += psum;
+      } else {
+        float psum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) psum += s[kb][r];
+        l_run += psum;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int d = db * 32 + lr;
+              const float a = d < D ? *(const float*)(sV + key * LROW + d * 4) : 0.0f;
+              oacc[db] = M::mma(a, s[kb][r], oacc[db]);
+            }
+          }
+      }
+    };
+
     fetch(0);
     stash(0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // One step of the key loop: prefetch tile kt + 1, consume tile kt, stash
+    // the prefetch into the other stage. Returns false on a bad block id.
+    auto step = [&](int kt, auto masked_tiles) {
       const int k0 = kt * kBlockN;
       const int stage = kt & 1;
       const bool more = kt + 1 < n_kt;
@@ -222,137 +362,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           const int hi = min(last_key, k0 + 2 * kBlockN - 1) >> shift;
           if (hi >= win_end) {   // uniform: every thread holds the same window
             load_window((k0 + kBlockN) >> shift);
-            if (s_bad) { poisoned = true; break; }
+            if (s_bad) return false;
           }
         }
         fetch(kt + 1);
       }
-
-      if (wave_live && k0 <= wave_pos_first + 31) {
-        const char* sK = s_kv[stage][0];
-        const char* sV = s_kv[stage][1];
-        // ---- S^T = K Q^T, two 32-key blocks
-        f32x16_t s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          f32x16_t acc = f32x16_t{};
-          const int row = kb * 32 + lr;
-#pragma unroll
-          for (int kk = 0; kk < KSTEPS; ++kk) {
-            typename M::Op a;
-            if constexpr (BF16) {
-              a = *(const bf16x8_t*)(sK + row * LROW + (2 * kk + hf) * 16);
-            } else {
-              a = *(const float*)(sK + row * LROW + (kk * 2 + hf) * 4);
-            }
-            acc = M::mma(a, qB[kk], acc);
-          }
-          s[kb] = acc;
+      if constexpr (decltype(masked_tiles)::value) {
+        if (wave_live && k0 <= wave_pos_first + 31) {
+          // Per wave: only tiles that cross its diagonal or the end of the keys.
+          const bool need_mask = (k0 + kBlockN - 1 > wave_pos_first) || (k0 + kBlockN > p.seq_kv);
+          tile(need_mask, k0, stage);
         }
-
-        // ---- causal / length mask on tiles that cross the diagonal or the end
-        const bool need_mask = (k0 + kBlockN - 1 > wave_pos_first) || (k0 + kBlockN > p.seq_kv);
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-              if (key > my_pos || key >= p.seq_kv) s[kb][r] = -INFINITY;
-            }
-        }
-
-        // ---- online softmax on this lane's row
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                           false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > kLazy) != 0) {   // wave-uniform
-          const float m_new = fmaxf(m_ref, mx);
-          const float alpha =
-              m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-          m_ref = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        }
-        // Key 0 is visible to every row, so m_ref is finite from the first tile on.
-        const float mc = m_ref == -INFINITY ? 0.0f : m_ref * c;
-        float psum = 0.0f;
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float sv = s[kb][r];
-              const float x = BF16 ? fmaf(sv, c, -mc) : (sv - m_ref) * c;
-              const float e = sv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x);
-              s[kb][r] = e;
-              psum += e;
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float x = BF16 ? fmaf(s[kb][r], c, -mc) : (s[kb][r] - m_ref) * c;
-              const float e = __builtin_amdgcn_exp2f(x);
-              s[kb][r] = e;
-              psum += e;
-            }
-        }
-        l_run += psum;
-
-        // ---- O^T += V^T P^T; accumulator register r of key block kb is key
-        //      32*kb + 8*(r/4) + 4*hf + r%4, and the V^T reads follow that order.
-        if constexpr (BF16) {
-          const int g16 = lane / 16, i16 = lane % 16;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-              bf16x8_t pb;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[kb][8 * mm + j];
-              // Lane (g16, i16) addresses row r0 + i16/4 at columns 4*(i16%4)..+3 of
-              // its 16-column slice and receives column (slice + i16) of rows r0..r0+3.
-              const int lo_row = kb * 32 + 16 * mm + 4 * hf + i16 / 4;
-              const int hi_row = lo_row + 8;
-#pragma unroll
-              for (int db = 0; db < DB; ++db) {
-                const int chunk = 4 * db + 2 * (g16 % 2) + (i16 % 4) / 2;
-                const bf16x4_t lo = ds_read_tr16(sV + lo_row * LROW + chunk * 16 + 8 * (i16 % 2));
-                const bf16x4_t hi = ds_read_tr16(sV + hi_row * LROW + chunk * 16 + 8 * (i16 % 2));
-                const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                oacc[db] = M::mma(a, pb, oacc[db]);
-              }
-            }
-          }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-#pragma unroll
-              for (int db = 0; db < DB; ++db) {
-                const int d = db * 32 + lr;
-                const float a = d < D ? *(const float*)(sV + key * LROW + d * 4) : 0.0f;
-                oacc[db] = M::mma(a, s[kb][r], oacc[db]);
-              }
-            }
-        }
+      } else {
+        tile(false, k0, stage);
       }
-
       if (more) stash(stage ^ 1);
       __syncthreads();
-    }
+      return true;
+    };
+
+    // Tiles below the diagonal of the wave's first row and wholly inside the
+    // keys need no mask for any of its rows: a loop of their own without the
+    // mask code; the rest (at most two tiles) take the masking loop. Every
+    // step has the same barriers whichever loop runs it, so the switch point
+    // may differ between the waves of the workgroup.
+    const int kt_open =
+        wave_live ? min(min((wave_pos_first + 1) / kBlockN, p.seq_kv / kBlockN), n_kt) : 0;
+    int kt = 0;
+    for (; kt < kt_open && !poisoned; ++kt) poisoned = !step(kt, std::false_type{});
+    for (; kt < n_kt && !poisoned; ++kt) poisoned = !step(kt, std::true_type{});
 
     if (!poisoned) {
       // ---- epilogue: l = both halves' shares; O^T / l -> o[b, row, h, :]
