@@ -50,11 +50,13 @@ def source_digest(kind):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the source."""
+def measured_traffic(workload, kind):
+    """HBM bytes per launch of one workload from committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration), or None
+    when the kernel source has changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)[kind]
+            t = json.load(f)[workload]
     except (OSError, KeyError, ValueError):
         return None
     if t.get("source_digest") != source_digest(kind):
@@ -216,7 +218,7 @@ def main():
         else:
             ach, peak, unit = w["flops"] / (r["us_avg"] * 1e-6) / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
         return {"bound": w["bound"], "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": measured_traffic(w["kind"]) if k != "chunked" else None,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(k, w["kind"]),
                 "kernel": w["kernel"], "us_per_launch": round(r["us_avg"], 2),
                 "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"]}
 
