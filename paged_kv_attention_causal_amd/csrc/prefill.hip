@@ -36,6 +36,7 @@ constexpr int kThreads = 256;
 constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;    // keys per tile
 constexpr int kBtWin = 256;    // block-table entries cached in LDS
+constexpr int kXcds = 8;       // accelerator complex dies, each with its own L2
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
 
 template <bool BF16>
@@ -97,10 +98,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   __shared__ int s_bt[PAGED ? kBtWin : 1];
   __shared__ int s_bad;
 
-  // Heaviest query tiles first; within a tile level, heads of one sequence.
+  // Work order: heaviest query tiles first; within a tile level, sequence,
+  // then head (the heads of one KV head adjacent). Workgroups are handed to
+  // the 8 XCDs round robin (XCD = id % 8), and each XCD has its own L2: so
+  // in every run of 8 x group ids, XCD x takes the group heads that share
+  // one KV head, which then read the same key tiles at the same time.
+  int work = blockIdx.x;
+  {
+    const int span = kXcds * p.group;
+    if ((int)(blockIdx.x / span + 1) * span <= (int)gridDim.x) {
+      const int g = blockIdx.x / span, x = blockIdx.x % kXcds, j = (blockIdx.x / kXcds) % p.group;
+      work = g * span + x * p.group + j;
+    }
+  }
   const int per_level = p.batch * p.n_heads;
-  const int qt = p.q_tiles - 1 - (int)(blockIdx.x / per_level);
-  const int rest = blockIdx.x % per_level;
+  const int qt = p.q_tiles - 1 - work / per_level;
+  const int rest = work % per_level;
   const int h = rest % p.n_heads;
   const int b = rest / p.n_heads;
   const int kvh = h / p.group;
