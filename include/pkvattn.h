@@ -180,9 +180,16 @@ size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int m
  *   latent  [batch, kv_capacity, kv_lora_rank + qk_rope_head_dim] (dtype).
  *   o_lat   [batch, n_heads, kv_lora_rank] (dtype, written): the softmax-weighted
  *           latent, before the per-head value up-projection.
- *   seq_lens, max_seq_len, workspace: as attn_decode_contig (the latent row of
- *           the current token is already appended).
- *   Built: PKVA_BF16 with kv_lora_rank 512, qk_rope_head_dim 64.
+ *   seq_lens, max_seq_len: as attn_decode_contig (the latent row of the
+ *           current token is already appended).
+ *   workspace: device memory of at least mla_decode_workspace_size(...) bytes,
+ *           16-byte aligned, owned by the caller, contents overwritten; may be
+ *           null when that size is 0 (the batch fills the GPU without
+ *           splitting the context). With a split context each piece leaves
+ *           its output divided by its own softmax sum in bf16 plus its max
+ *           and sum in fp32, and a second kernel merges the pieces.
+ *   Built: PKVA_BF16 with kv_lora_rank 512, qk_rope_head_dim 64, n_heads a
+ *           multiple of 32 that is at most 128 or a multiple of 128.
  */
 int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_lat,
                       int batch, int n_heads, int kv_lora_rank, int qk_rope_head_dim,

@@ -90,7 +90,7 @@ struct MlaShape {
 MlaShape mla_shape(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
   MlaShape s;
   const int tile = pkva::mla_tile_tokens();
-  const int64_t items = (int64_t)batch * (n_heads / pkva::mla_heads_per_group());
+  const int64_t items = (int64_t)batch * (n_heads / pkva::mla_heads_per_group(n_heads));
   int64_t nsplit = items >= kMlaTargetGroups ? 1 : ceil_div(kMlaTargetGroups, items);
   const int64_t max_split = ceil_div(max_seq_len, tile);
   if (nsplit > max_split) nsplit = max_split;
@@ -98,8 +98,9 @@ MlaShape mla_shape(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
   const int64_t per = ceil_div(ceil_div(max_seq_len, nsplit), tile) * tile;
   s.split_tokens = (int)per;
   s.nsplit = (int)ceil_div(max_seq_len, per);
+  // per split and head: kv_lora_rank bf16 (O / l), then m and l in fp32
   s.ws_bytes = s.nsplit > 1
-                   ? (size_t)((int64_t)batch * s.nsplit * n_heads * (kv_lora_rank + 2) * (int64_t)sizeof(float))
+                   ? (size_t)((int64_t)batch * s.nsplit * n_heads * (kv_lora_rank * 2 + 2 * 4))
                    : 0;
   return s;
 }
@@ -242,7 +243,7 @@ int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* 
 
 size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
   if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || max_seq_len < 1) return 0;
-  if (n_heads % pkva::mla_heads_per_group() != 0) return 0;
+  if (!pkva::mla_supported(true, kv_lora_rank, 64, n_heads)) return 0;
   return mla_shape(batch, n_heads, kv_lora_rank, max_seq_len).ws_bytes;
 }
 
@@ -259,7 +260,7 @@ int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_
   if (!pkva::mla_supported(dtype == PKVA_BF16, kv_lora_rank, qk_rope_head_dim, n_heads))
     return PKVA_EUNSUPPORTED;
   const MlaShape sh = mla_shape(batch, n_heads, kv_lora_rank, max_seq_len);
-  if ((int64_t)batch * (n_heads / pkva::mla_heads_per_group()) * sh.nsplit > kMaxGrid)
+  if ((int64_t)batch * (n_heads / pkva::mla_heads_per_group(n_heads)) * sh.nsplit > kMaxGrid)
     return PKVA_EINVAL;
   if (sh.ws_bytes > 0) {
     if (!workspace || workspace_bytes < sh.ws_bytes) return PKVA_EWORKSPACE;
@@ -268,8 +269,9 @@ int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_
 
   pkva::MlaParams p{};
   p.q = q_abs; p.latent = latent; p.o = o_lat; p.seq_lens = seq_lens;
-  p.ws_o = (float*)workspace;
-  p.ws_ml = sh.ws_bytes > 0 ? p.ws_o + (int64_t)batch * sh.nsplit * n_heads * kv_lora_rank : nullptr;
+  p.ws_o = (__bf16*)workspace;
+  p.ws_ml = sh.ws_bytes > 0 ? (float*)(p.ws_o + (int64_t)batch * sh.nsplit * n_heads * kv_lora_rank)
+                            : nullptr;
   p.batch = batch; p.n_heads = n_heads; p.kv_capacity = kv_capacity; p.max_seq_len = max_seq_len;
   p.nsplit = sh.nsplit; p.split_tokens = sh.split_tokens;
   p.scale_log2 = attention_scale * pkva::kLog2eHost;

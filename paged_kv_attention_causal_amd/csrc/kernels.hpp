@@ -65,15 +65,15 @@ struct MlaParams {
   const void* latent;         // [batch, cap, R + P]
   void* o;                    // [batch, n_heads, R]
   const int32_t* seq_lens;
-  float* ws_o;                // [batch, nsplit, n_heads, R]   (nsplit > 1 only)
-  float* ws_ml;               // [batch, nsplit, n_heads, 2]
+  __bf16* ws_o;               // [batch, nsplit, n_heads, R] O / l of each split (nsplit > 1 only)
+  float* ws_ml;               // [batch, nsplit, n_heads, 2] (m * scale * log2e, l)
   int batch, n_heads, kv_capacity, max_seq_len;
   int nsplit, split_tokens;   // context split: nsplit pieces of split_tokens tokens
   float scale_log2;
 };
 
 bool mla_supported(bool bf16, int kv_lora_rank, int rope_dim, int n_heads);
-int mla_heads_per_group();
+int mla_heads_per_group(int n_heads);   // heads served by one workgroup
 int mla_tile_tokens();
 int launch_mla(const MlaParams& p, hipStream_t stream);
 

@@ -2,283 +2,502 @@
 // src/mla/mod.rs, absorbed_attention and the MlaKvB doc): every head h
 // attends over the sequence's cached latent rows [c | k_rot] (width R + P)
 // with its absorbed query q_abs[h]; the value is each row's first R entries.
-// It is multi-query attention with one shared KV head, so the latent tile is
-// loaded once per workgroup and serves all of its heads.
+// It is multi-query attention with one shared KV head, so a latent tile is
+// staged once per workgroup and serves all of its heads.
 //
-// One workgroup = 4 waves = 16 heads of one sequence over a token range.
-// 64-token latent tiles move through a two-stage LDS ring (row-major, padded
-// rows): the next tile is loaded into registers while the current one is
-// consumed. Per tile:
-//   wave w computes S^T = L Q^T for tokens 16w..16w+15 (16x16x32 bf16 MFMA,
-//   Q^T in registers) and writes the raw scores to LDS;
-//   every wave then reads all 64 scores of its lane's head, runs the same
-//   online-softmax update (identical in all four waves), and accumulates its
-//   own quarter of the value width, O^T[128w .. 128w+127] += V^T P^T, with
-//   the V^T operand read from the row-major tile by ds_read_b64_tr_b16.
-// When the batch already fills the chip each workgroup takes a whole
-// sequence and writes o_lat directly; otherwise the context is split and
-// mla_combine merges the pieces in split order.
+// One workgroup = up to 128 heads of one sequence over a range of its
+// context, one wave per 32 heads. A latent byte read from LDS by a wave feeds
+// its 32 heads (S^T = L Q^T and O^T += V^T P^T on 32x32x16 MFMAs): per wave
+// Q^T stays in VGPRs (144) and O^T for 32 heads x 512 values in the 256
+// AGPRs, so one wave per SIMD. The context of a sequence is split over
+// workgroups to fill the chip; mla_combine merges the pieces.
+//
+// 32-token latent tiles (36 KB) are copied global -> LDS by the DMA path
+// (global_load_lds_dwordx4) three tiles ahead into a four-stage ring. Rows
+// are 1152 bytes with the 16-byte chunks XOR-swizzled by 2*(r%4) + (r/4)%2
+// inside each group of 8: a DMA op fills 1 KB of the tile with any
+// lane-to-chunk map, and both operand reads stay free of bank conflicts.
+//
+// Per step a wave takes the softmax of tile i (S^T computed in the previous
+// step), then runs the 36 MFMAs of S^T for tile i + 1 interleaved with the
+// 32 of O^T += V^T P^T for tile i. In the accumulator layout lane l owns head
+// l % 32 and 16 of the tile's tokens (the other 16 in lane l ^ 32): the max
+// needs one v_permlane32_swap, the sum stays per lane until the end; P goes
+// from the accumulator registers straight to the B operand, and the V^T
+// operand comes from the row-major tile through ds_read_b64_tr_b16. The
+// running max moves only when a head's max grows by more than 2^8 in the
+// exp2 domain (then O and l are rescaled).
 #include "common.hpp"
 #include "kernels.hpp"
+
+#include <type_traits>
 
 namespace pkva {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kHeads = 16;       // heads per workgroup
-constexpr int kTile = 64;        // tokens per LDS tile
-constexpr int kR = 512;          // kv_lora_rank
-constexpr int kP = 64;           // qk_rope_head_dim
-constexpr int kW = kR + kP;      // latent row width
-constexpr int kLatStr = kW + 8;  // padded row stride of the row-major tile
-constexpr int kSStr = kTile + 4;
-constexpr int kKSteps = kW / 32; // MFMA k-steps for the scores (18)
-constexpr int kDPerWave = kR / 4;
+constexpr int kHW = 32;           // heads per wave
+constexpr int kMaxWaves = 4;      // waves (head groups of 32) per workgroup
+constexpr int kTile = 32;         // tokens per tile
+constexpr int kStages = 4;
+constexpr int kPrefetch = 3;      // tiles in flight ahead of the one consumed
+constexpr int kR = 512;           // kv_lora_rank
+constexpr int kP = 64;            // qk_rope_head_dim
+constexpr int kW = kR + kP;       // latent row width
+constexpr int kRowB = kW * 2;     // 1152 bytes
+constexpr int kChunks = kW / 8;   // 16-byte chunks per row (72)
+constexpr int kTileB = kTile * kRowB;
+constexpr int kDmaTile = kTileB / 1024;   // 1 KB DMA ops per tile (36)
+constexpr int kKSteps = kW / 16;  // 16-deep MFMA steps of the scores (36)
+constexpr int kDB = kR / 32;      // 32-row blocks of O^T (16)
+constexpr float kLazy = 8.0f;
+constexpr int kXcds = 8;          // accelerator complex dies, each with its own L2
+constexpr int kAhead = 4;        // MFMA pairs whose operands are read ahead
+static_assert(kTileB % 1024 == 0 && kChunks % 8 == 0, "tile geometry");
+static_assert(kKSteps >= 2 * kDB, "value MFMAs interleave with the score MFMAs");
 
-__device__ __forceinline__ f32x4_t mma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16_t mma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Physical workgroup id -> logical item, so that the items that read the same
-// sequence's latent (its head groups and splits) run on one XCD and share its
-// L2. Workgroups are dispatched to the 8 XCDs round-robin by id.
-__device__ __forceinline__ int xcd_logical(int i, int n) {
-  constexpr int kXcd = 8;
-  if (n % kXcd != 0) return i;
-  return (i % kXcd) * (n / kXcd) + i / kXcd;
+// The score MFMAs, written so their accumulator lives in VGPRs: the 256 AGPRs
+// hold O^T, and with the compiler's choice (AGPR accumulators for every MFMA
+// of the kernel) the scores would displace O^T blocks every tile. Dependent
+// MFMAs on one accumulator need no wait states; a VALU read of the result
+// does (see score_wait).
+__device__ __forceinline__ f32x16_t mma_v_first(bf16x8_t a, bf16x8_t b) {
+  f32x16_t d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
 }
+__device__ __forceinline__ void mma_v(f32x16_t& d, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// Wait states between the last score MFMA (8 passes) and a VALU access of its
+// accumulator, which the compiler cannot see through the inline assembly.
+__device__ __forceinline__ void score_wait() { asm volatile("s_nop 15\n\ts_nop 7" ::: "memory"); }
 
 // Transposed LDS read: four consecutive rows of one 16-bit column per lane.
-__device__ __forceinline__ bf16x4_t ds_read_tr16(const void* p) {
+__device__ __forceinline__ bf16x4_t ds_read_tr16(const char* p) {
   typedef __attribute__((ext_vector_type(4))) short s16x4;
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+      (lds_s16x4*)(__attribute__((address_space(3))) const char*)(p));
   return __builtin_bit_cast(bf16x4_t, v);
 }
 
-__global__ __launch_bounds__(kThreads) void mla_kernel(MlaParams p) {
-  constexpr int kRowB = kLatStr * 2;                    // padded row bytes in LDS
-  constexpr int kChunks = kTile * (kW / 8);             // 16-byte chunks per tile
-  constexpr int kLpt = kChunks / kThreads;              // loads per thread per tile
-  static_assert(kChunks % kThreads == 0, "tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) __bf16 sLat[2][kTile * kLatStr];
-  __shared__ __attribute__((aligned(16))) float sS[kHeads * kSStr];
+__device__ __forceinline__ int swz(int r) { return 2 * (r % 4) + (r / 4) % 2; }
 
-  const int n_hg = p.n_heads / kHeads;
-  const int n_items = p.batch * n_hg * p.nsplit;
-  const int item = xcd_logical(blockIdx.x, n_items);
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in [15:14]; the others at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One 16-byte-per-lane DMA copy global -> LDS from a uniform base plus a
+// per-lane 32-bit offset: lane i's 16 bytes land at LDS byte lds + 16 * i (M0
+// holds the wave's base; one wait state after writing it). Issued as inline assembly so the compiler does not track it: it would
+// otherwise wait for every copy in flight before each LDS read it cannot
+// prove disjoint. Completion is awaited with counted vmcnt waits.
+// The base and the LDS address are uniform by construction; passing them
+// through readfirstlane lets the compiler prove it, so they always get the
+// scalar registers the instruction needs.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"((const void*)(uintptr_t)sb), "s"(sl)
+               : "memory", "m0");
+}
+
+// acc *= alpha with acc kept in accumulation registers (read, scale and write
+// back in place; plain VALU arithmetic on them makes the compiler move all of
+// them through VGPRs on every loop trip). The s_nops cover the MFMA-write to
+// v_accvgpr_read and v_accvgpr_write to MFMA wait states.
+__device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kDB], float alpha) {
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = acc[db][i], t;
+      asm volatile(
+          "v_accvgpr_read_b32 %1, %0\n\t"
+          "v_mul_f32 %1, %1, %2\n\t"
+          "v_accvgpr_write_b32 %0, %1"
+          : "+a"(x), "=&v"(t)
+          : "v"(alpha));
+      acc[db][i] = x;
+    }
+  asm volatile("s_nop 7" ::: "memory");
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
+  static_assert(kDmaTile % NW == 0, "every thread copies the same number of chunks");
+  constexpr int kDmaPerThread = kDmaTile / NW;
+  __shared__ __attribute__((aligned(1024))) char s_lat[kStages * kTileB];
+
+  // Work item = (sequence, head group, split), split fastest. Workgroups go
+  // to the 8 XCDs round robin (XCD = id % 8); a run of consecutive items
+  // per XCD keeps the pieces of one sequence on one L2, which then reads the
+  // sequence's queries from memory once.
+  const int n_hg = p.n_heads / (kHW * NW);
+  int item = blockIdx.x;
+  if (gridDim.x % kXcds == 0) item = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
   const int split = item % p.nsplit;
   const int hg = (item / p.nsplit) % n_hg;
   const int b = item / (p.nsplit * n_hg);
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-  const int l16 = lane % 16, quad = lane / 16;
-  const int head = hg * kHeads + l16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int lr = lane % 32, hf = lane / 32;
+  const int head = (hg * NW + wave) * kHW + lr;
 
   const int L = p.seq_lens[b];
   const bool bad = L < 1 || L > p.max_seq_len;
   const int t_begin = split * p.split_tokens;
   const int t_end = bad ? 0 : min(L, t_begin + p.split_tokens);
+  const int n_t = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
+  const char* lat = (const char*)p.latent + (int64_t)b * p.kv_capacity * kRowB;
 
-  // Q^T as the B operand: lane holds head l16, dims 32*kk + 8*quad .. +7.
-  bf16x8_t qB[kKSteps];
+  // Copy tile i (tokens t_begin + 32 i ..) into its stage. DMA op j of this
+  // wave covers bytes [1024 ins, +1024) of the tile, ins = wave + NW * j,
+  // i.e. chunk slots 64 ins + lane in row-major order; the lane brings the
+  // chunk the swizzle puts there, at byte dma_off[j] of the tile's rows in
+  // global memory. Rows past t_end copy row t_end - 1 instead (their scores
+  // are masked; a NaN beyond the context must not reach P * V), so every
+  // thread issues the same number of copies per tile and the counted waits
+  // hold.
+  uint32_t dma_off[kDmaPerThread];
+#pragma unroll
+  for (int j = 0; j < kDmaPerThread; ++j) {
+    const int q = 64 * (wave + NW * j) + lane;
+    const int row = q / kChunks, slot = q % kChunks;
+    dma_off[j] = (uint32_t)(row * kRowB + 16 * (slot ^ swz(row)));
+  }
+  auto issue = [&](int i) {
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(s_lat) +
+                        (uint32_t)((i % kStages) * kTileB);
+    const int t0 = t_begin + kTile * i;
+    const char* base = lat + (int64_t)t0 * kRowB;
+    if (t0 + kTile <= t_end) {
+#pragma unroll
+      for (int j = 0; j < kDmaPerThread; ++j) dma16(base, dma_off[j], st + 1024u * (wave + NW * j));
+    } else {
+      const int last = t_end - 1 - t0;   // last live row of the tile
+#pragma unroll
+      for (int j = 0; j < kDmaPerThread; ++j) {
+        const int row = (int)(dma_off[j] / kRowB);
+        const uint32_t off = dma_off[j] - (uint32_t)((row - min(row, last)) * kRowB);
+        dma16(base, off, st + 1024u * (wave + NW * j));
+      }
+    }
+  };
+  // publish(i) runs when the tiles up to min(i + kPrefetch - 1, n_t - 1) are
+  // issued: wait until at most the later tiles' copies are in flight (vmcnt
+  // counts in issue order), then the barrier publishes tile i to every wave
+  // and retires every read of the stage the next copy reuses.
+  auto publish = [&](int i) {
+    const int later = max(0, min(i + kPrefetch - 1, n_t - 1) - i);
+    static_assert(kPrefetch - 1 <= 2, "extend the wait cases");
+    // (vmcnt holds at most 63: waiting for fewer in flight is also correct.)
+    constexpr int kOne = kDmaPerThread < 63 ? kDmaPerThread : 63;
+    constexpr int kTwo = 2 * kDmaPerThread < 63 ? 2 * kDmaPerThread : 63;
+    if (later == 0) {
+      wait_vmcnt<0>();
+    } else if (later == 1) {
+      wait_vmcnt<kOne>();
+    } else {
+      wait_vmcnt<kTwo>();
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Per-lane LDS offsets inside a tile (the rest is an immediate):
+  //   K fragment of S^T (A operand): row lr, chunk 2*kk + hf swizzled by
+  //   swz(lr), which flips kk bits 0-1: one base per kk % 4;
+  //   V^T fragment: lane (g16, i16) reads row 16*mm + 4*hf + i16/4 (+8 for
+  //   the upper half), chunk 4*db + 2*(g16%2) + (i16%4)/2, half i16 % 2; the
+  //   swizzle flips db parity for half the lanes: one base per db parity.
+  const int g16 = lane / 16, i16 = lane % 16;
+  int k_base[4];
   {
-    const __bf16* qg = (const __bf16*)p.q + ((int64_t)b * p.n_heads + head) * kW + 8 * quad;
+    const int sk = swz(lr);
+    const int lb = lr * kRowB + 16 * (hf ^ (sk & 1));
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) qB[kk] = *(const bf16x8_t*)(qg + 32 * kk);
+    for (int j = 0; j < 4; ++j) k_base[j] = lb + 32 * ((j ^ (sk >> 1)) - j);
+  }
+  int v_even, v_odd;
+  {
+    const int r = 4 * hf + i16 / 4;
+    const int sv = swz(r);
+    const int cl = 2 * (g16 % 2) + (i16 % 4) / 2;
+    const int lb = r * kRowB + 16 * (cl ^ (sv & 3)) + 8 * (i16 % 2);
+    v_even = lb + 64 * (sv >> 2);
+    v_odd = lb - 64 * (sv >> 2);
   }
 
-  f32x4_t oacc[kDPerWave / 16];
+  bf16x8_t qB[kKSteps];   // Q^T as the B operand: head lr, dims 16*kk + 8*hf .. +7
+  f32x16_t oacc[kDB];
 #pragma unroll
-  for (int db = 0; db < kDPerWave / 16; ++db) oacc[db] = f32x4_t{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  for (int db = 0; db < kDB; ++db) oacc[db] = f32x16_t{};
+  float m_ref = -INFINITY, l_run = 0.0f;
   const float c = p.scale_log2;
-  const char* lat = (const char*)p.latent + (int64_t)b * p.kv_capacity * (kW * 2);
+  bf16x8_t pb[2];   // P^T of the tile being consumed, [16-token half]
 
-  // Tile fetch into registers (tokens past t_end read as zero) and stash to LDS.
-  uint4 st[kLpt];
-  auto fetch = [&](int t0) {
+  // S^T of the tile in stage `stage` (36 dependent MFMAs), interleaved with
+  // O^T += V^T P^T for the tile in stage `pv_stage` (32 independent ones)
+  // when WITH_PV: the value MFMAs fill the latency between the score MFMAs.
+  // Operand reads run kAhead MFMA pairs ahead through register rings;
+  // the scheduling barriers keep the compiler from hoisting all 68 reads
+  // (which would not fit in registers).
+  auto read_k = [&](const char* sk, int kk) {
+    return *(const bf16x8_t*)(sk + k_base[kk % 4] + 32 * kk);
+  };
+  auto read_v = [&](const char* sv, int idx) {   // idx = 16 * mm + db
+    const int mm = idx / kDB, db = idx % kDB;
+    const char* vb = sv + ((db & 1) ? v_odd : v_even) + 16 * mm * kRowB + 64 * db;
+    const bf16x4_t lo = ds_read_tr16(vb);
+    const bf16x4_t hi = ds_read_tr16(vb + 8 * kRowB);
+    return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto scores_and_values = [&](f32x16_t& s, int stage, int pv_stage, auto with_pv) {
+    constexpr bool PV = decltype(with_pv)::value;
+    const char* sk = s_lat + stage * kTileB;
+    const char* sv = s_lat + pv_stage * kTileB;
+    bf16x8_t kr[kAhead + 1], vr[kAhead + 1];
 #pragma unroll
-    for (int j = 0; j < kLpt; ++j) {
-      const int ci = tid + kThreads * j;
-      const int row = ci / (kW / 8), cc = ci % (kW / 8);
-      const int t = t0 + row;
-      st[j] = make_uint4(0, 0, 0, 0);
-      if (t < t_end) st[j] = *(const uint4*)(lat + (int64_t)t * (kW * 2) + cc * 16);
+    for (int j = 0; j < kAhead; ++j) kr[j] = read_k(sk, j);
+    if constexpr (PV) {
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) vr[j] = read_v(sv, j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      if (kk + kAhead < kKSteps) kr[(kk + kAhead) % (kAhead + 1)] = read_k(sk, kk + kAhead);
+      if (PV && kk + kAhead < 2 * kDB) vr[(kk + kAhead) % (kAhead + 1)] = read_v(sv, kk + kAhead);
+      if (kk == 0) {
+        s = mma_v_first(kr[0], qB[0]);
+      } else {
+        mma_v(s, kr[kk % (kAhead + 1)], qB[kk]);
+      }
+      if (PV && kk < 2 * kDB) {
+        const int mm = kk / kDB, db = kk % kDB;
+        oacc[db] = mma(vr[kk % (kAhead + 1)], pb[mm], oacc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto stash = [&](int stage) {
+  // O^T += V^T P^T alone (the last tile of the range).
+  auto values = [&](int pv_stage) {
+    const char* sv = s_lat + pv_stage * kTileB;
+    bf16x8_t vr[kAhead + 1];
 #pragma unroll
-    for (int j = 0; j < kLpt; ++j) {
-      const int ci = tid + kThreads * j;
-      const int row = ci / (kW / 8), cc = ci % (kW / 8);
-      *(uint4*)((char*)sLat[stage] + row * kRowB + cc * 16) = st[j];
+    for (int j = 0; j < kAhead; ++j) vr[j] = read_v(sv, j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int idx = 0; idx < 2 * kDB; ++idx) {
+      if (idx + kAhead < 2 * kDB) vr[(idx + kAhead) % (kAhead + 1)] = read_v(sv, idx + kAhead);
+      oacc[idx % kDB] = mma(vr[idx % (kAhead + 1)], pb[idx / kDB], oacc[idx % kDB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (t_begin < t_end) {
-    fetch(t_begin);
-    stash(0);
-    __syncthreads();
-  }
-  int stage = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile, stage ^= 1) {
-    const bool more = t0 + kTile < t_end;
-    if (more) fetch(t0 + kTile);
-    const char* tile = (const char*)sLat[stage];
+  // Softmax of tile i (scores in s): mask tokens past t_end, lazy max,
+  // P in bf16 (pb) and the row sum of the same rounded values. Accumulator
+  // register r holds token 32 i + 8*(r/4) + 4*hf + r%4 of the range.
+  const uint32_t ones = 0x3f803f80u;
+  auto softmax = [&](f32x16_t& s, int i) {
+    score_wait();
+    const int t0 = t_begin + kTile * i;
+    if (t0 + kTile > t_end) {
+      const int lim = t_end - 1 - (t0 + 4 * hf);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + (r % 4) > lim) s[r] = -INFINITY;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2)
+      m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, s[r]), s[r + 1]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                     false, false);
+    m = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    // Token t0 is live for every head, so m is finite.
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64((m - m_ref) * c > kLazy) != 0, 0)) {
+      const float m_new = fmaxf(m_ref, m);
+      const float alpha = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+      m_ref = m_new;
+      l_run *= alpha;
+      scale_acc(oacc, alpha);
+    }
+    const float mc = m_ref * c;
+    float ps = 0.0f;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        pb[mm][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * mm + j], c, -mc));
+      const auto w = __builtin_bit_cast(uint4, pb[mm]);
+      ps = dot2_bf16(w.x, ones, ps);
+      ps = dot2_bf16(w.y, ones, ps);
+      ps = dot2_bf16(w.z, ones, ps);
+      ps = dot2_bf16(w.w, ones, ps);
+    }
+    l_run += ps;
+  };
 
-    // ---- raw scores for tokens 16*wave .. +15 of the tile
+  if (n_t > 0) {
+    // Prologue: tiles 0 .. kPrefetch-1 in flight, Q^T loaded meanwhile, then
+    // every load done (no load the compiler tracks is pending in the loop),
+    // tile 0 published, its scores.
+    for (int i = 0; i < kPrefetch && i < n_t; ++i) issue(i);
     {
-      f32x4_t acc = f32x4_t{};
-      const char* lrow = tile + (16 * wave + l16) * kRowB + 16 * quad;
+      const __bf16* qg = (const __bf16*)p.q + ((int64_t)b * p.n_heads + head) * kW + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) acc = mma16(*(const bf16x8_t*)(lrow + 64 * kk), qB[kk], acc);
-      // accumulator: lane l16 = head, rows = tokens 16*wave + 4*quad + r
-      *(f32x4_t*)(sS + l16 * kSStr + 16 * wave + 4 * quad) = acc;
+      for (int kk = 0; kk < kKSteps; ++kk) qB[kk] = *(const bf16x8_t*)(qg + 16 * kk);
     }
-    __syncthreads();
+    wait_vmcnt<0>();
+    publish(0);
+    // One score tile is enough: the softmax turns it into P (pb) before the
+    // next tile's scores are computed into the same registers.
+    f32x16_t sc;
+    scores_and_values(sc, 0, 0, std::false_type{});
 
-    // ---- online softmax over the tile's 64 tokens (same in every wave)
-    float sv[2][8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const float* srow = sS + l16 * kSStr + 32 * pp + 8 * quad;
-      const f32x4_t a = *(const f32x4_t*)srow;
-      const f32x4_t b4 = *(const f32x4_t*)(srow + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[pp][j] = a[j];
-        sv[pp][4 + j] = b4[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = t0 + 32 * pp + 8 * quad + j;
-        if (t >= t_end) sv[pp][j] = -INFINITY;
-        mx = fmaxf(mx, sv[pp][j]);
-      }
+    // Step i: copy tile i + kPrefetch; softmax of tile i; publish tile i + 1;
+    // its scores together with the values of tile i. The last tile is peeled
+    // off (no next tile), so the loop has no branch that would make the
+    // compiler copy O^T between register sets.
+    for (int i = 0; i + 1 < n_t; ++i) {
+      if (i + kPrefetch < n_t) issue(i + kPrefetch);
+      softmax(sc, i);
+      publish(i + 1);
+      scores_and_values(sc, (i + 1) % kStages, i % kStages, std::true_type{});
     }
-    mx = fmaxf(mx, xchg<4>(mx));
-    mx = fmaxf(mx, xchg<5>(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = m_new * c;   // finite: the tile holds at least one live token
-    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(m_run, c, -mc));
-    m_run = m_new;
-    float psum = 0.0f;
-    bf16x8_t pB[2];
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = sv[pp][j];
-        const float e = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(x, c, -mc));
-        psum += e;
-        pB[pp][j] = (__bf16)e;
-      }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int db = 0; db < kDPerWave / 16; ++db) oacc[db] *= alpha;
-
-    // ---- O^T[this wave's quarter] += V^T P^T over tokens 32*pp + 8*quad + j.
-    // Lane (quad, l16) addresses row k0 + l16/4 at columns 4*(l16%4)..+3 of a
-    // 16-column slice and receives column (slice + l16) of rows k0 .. k0+3.
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int r0 = 32 * pp + 8 * quad + l16 / 4;
-#pragma unroll
-      for (int db = 0; db < kDPerWave / 16; ++db) {
-        const int col = kDPerWave * wave + 16 * db + 4 * (l16 % 4);
-        const bf16x4_t lo = ds_read_tr16(tile + r0 * kRowB + col * 2);
-        const bf16x4_t hi = ds_read_tr16(tile + (r0 + 4) * kRowB + col * 2);
-        const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = mma16(a, pB[pp], oacc[db]);
-      }
-    }
-    if (more) stash(stage ^ 1);
-    __syncthreads();
+    softmax(sc, n_t - 1);
+    values((n_t - 1) % kStages);
   }
 
-  // ---- epilogue: the head's sum is spread over the 4 lanes l16 + 16*quad
-  float l_tot = l_run + xchg<4>(l_run);
-  l_tot = l_tot + xchg<5>(l_tot);
-  const int d0 = kDPerWave * wave + 4 * quad;
+  // ---- epilogue: l = both halves' shares. The scaled O^T goes through LDS
+  // (free once every wave is past its last tile) so that every store writes
+  // one head's 1 KB row: row h of the workgroup at byte h * kOutRow (padded:
+  // the 32 heads a wave writes at once spread over the banks).
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                    false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+  float inv;
+  __bf16* dst;   // the workgroup's first row (head hg * 32 * NW)
   if (p.nsplit == 1) {
-    __bf16* og = (__bf16*)p.o + ((int64_t)b * p.n_heads + head) * kR;
-    if (bad) {
-#pragma unroll
-      for (int db = 0; db < kDPerWave / 16; ++db) {
-        const bf16x4_t w = {(__bf16)__builtin_nanf(""), (__bf16)__builtin_nanf(""),
-                            (__bf16)__builtin_nanf(""), (__bf16)__builtin_nanf("")};
-        *(bf16x4_t*)(og + d0 + 16 * db) = w;
-      }
-      return;
-    }
-    const float inv = 1.0f / l_tot;
-#pragma unroll
-    for (int db = 0; db < kDPerWave / 16; ++db) {
-      const bf16x4_t w = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
-                          (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
-      *(bf16x4_t*)(og + d0 + 16 * db) = w;
-    }
+    inv = bad ? __builtin_nanf("") : 1.0f / l_tot;
+    dst = (__bf16*)p.o + ((int64_t)b * p.n_heads + hg * kHW * NW) * kR;
   } else {
-    // Partial of this split: unnormalised O, m in the log2 domain, l.
+    // Partial of this split: O / l in bf16 (half the traffic of the fp32
+    // numerator, one more rounding of the size of the output's own), then
+    // m in the log2 domain and l in fp32.
+    inv = n_t > 0 ? 1.0f / l_tot : 0.0f;
     const int64_t w = ((int64_t)b * p.nsplit + split) * p.n_heads + head;
-    float* wo = p.ws_o + w * kR;
-#pragma unroll
-    for (int db = 0; db < kDPerWave / 16; ++db)
-      *(f32x4_t*)(wo + d0 + 16 * db) = oacc[db];
-    if (wave == 0 && quad == 0) {
-      const bool live = t_begin < t_end;
-      p.ws_ml[w * 2 + 0] = live ? m_run * c : -INFINITY;
-      p.ws_ml[w * 2 + 1] = live ? l_tot : 0.0f;
+    dst = p.ws_o + (((int64_t)b * p.nsplit + split) * p.n_heads + hg * kHW * NW) * kR;
+    if (hf == 0) {
+      p.ws_ml[w * 2 + 0] = n_t > 0 ? m_ref * c : -INFINITY;
+      p.ws_ml[w * 2 + 1] = n_t > 0 ? l_tot : 0.0f;
     }
+  }
+  constexpr int kOutRow = kR * 2 + 8;
+  static_assert(kHW * kMaxWaves * kOutRow <= kStages * kTileB, "output rows fit in the ring");
+  __syncthreads();   // every wave is done with the latent tiles
+  // Accumulator register r of block db holds value 32*db + 8*(r/4) + 4*hf + r%4.
+  char* my_rows = s_lat + (wave * kHW) * kOutRow;
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const bf16x4_t v = {(__bf16)(oacc[db][4 * g4 + 0] * inv), (__bf16)(oacc[db][4 * g4 + 1] * inv),
+                          (__bf16)(oacc[db][4 * g4 + 2] * inv), (__bf16)(oacc[db][4 * g4 + 3] * inv)};
+      *(bf16x4_t*)(my_rows + lr * kOutRow + 2 * (32 * db + 8 * g4 + 4 * hf)) = v;
+    }
+  // A wave reads back only its own rows: its LDS writes are complete once
+  // lgkmcnt drains, which the compiler waits for before the reads.
+  __bf16* my_dst = dst + (int64_t)(wave * kHW) * kR;
+#pragma unroll 4
+  for (int r = 0; r < kHW; ++r) {
+    const uint4 v = *(const uint4*)(my_rows + r * kOutRow + 16 * lane);
+    *(uint4*)(my_dst + (int64_t)r * kR + 8 * lane) = v;
   }
 }
 
-// Merge the splits of one (sequence, head) in split order.
-__global__ __launch_bounds__(kThreads) void mla_combine(MlaParams p) {
-  const int b = blockIdx.x / p.n_heads;
-  const int h = blockIdx.x % p.n_heads;
+// Merge the splits of each (sequence, head) in split order: 128 threads per
+// head, four values per thread. Split s contributes 2^(m_s - M) * l_s times
+// its normalised partial.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineHeads = kCombineThreads / (kR / 4);   // heads per workgroup
+__global__ __launch_bounds__(kCombineThreads) void mla_combine(MlaParams p) {
+  const int hh = threadIdx.x / (kR / 4);
+  const int d = 4 * (threadIdx.x % (kR / 4));
+  const int bh = blockIdx.x * kCombineHeads + hh;   // b * n_heads + h
+  const int b = bh / p.n_heads, h = bh % p.n_heads;
   const int L = p.seq_lens[b];
   const bool bad = L < 1 || L > p.max_seq_len;
   const int nsp = bad ? 0 : (L + p.split_tokens - 1) / p.split_tokens;
+  const int64_t w0 = (int64_t)b * p.nsplit * p.n_heads + h;   // split s: w0 + s * n_heads
   float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, p.ws_ml[(((int64_t)b * p.nsplit + s) * p.n_heads + h) * 2]);
-  for (int d = threadIdx.x; d < kR; d += kThreads) {
-    float out = __builtin_nanf("");
-    if (!bad) {
-      float num = 0.0f, den = 0.0f;
-      for (int s = 0; s < nsp; ++s) {
-        const int64_t w = ((int64_t)b * p.nsplit + s) * p.n_heads + h;
-        const float wt = __builtin_amdgcn_exp2f(p.ws_ml[w * 2] - M);
-        num = fmaf(wt, p.ws_o[w * kR + d], num);
-        den = fmaf(wt, p.ws_ml[w * 2 + 1], den);
-      }
-      out = num / den;
-    }
-    ((__bf16*)p.o)[((int64_t)b * p.n_heads + h) * kR + d] = (__bf16)out;
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, p.ws_ml[(w0 + (int64_t)s * p.n_heads) * 2]);
+  f32x4_t num = f32x4_t{};
+  float den = 0.0f;
+  for (int s = 0; s < nsp; ++s) {
+    const int64_t w = w0 + (int64_t)s * p.n_heads;
+    const float wl = __builtin_amdgcn_exp2f(p.ws_ml[w * 2] - M) * p.ws_ml[w * 2 + 1];
+    den += wl;
+    const bf16x4_t o = *(const bf16x4_t*)(p.ws_o + w * kR + d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) num[j] = fmaf(wl, (float)o[j], num[j]);
   }
+  const float inv = bad ? __builtin_nanf("") : 1.0f / den;
+  const bf16x4_t out = {(__bf16)(num[0] * inv), (__bf16)(num[1] * inv), (__bf16)(num[2] * inv),
+                        (__bf16)(num[3] * inv)};
+  *(bf16x4_t*)((__bf16*)p.o + (int64_t)bh * kR + d) = out;
+}
+
+template <int NW>
+int launch_nw(const MlaParams& p, hipStream_t stream) {
+  const int n_items = p.batch * (p.n_heads / (kHW * NW)) * p.nsplit;
+  hipLaunchKernelGGL(mla_kernel<NW>, dim3(n_items), dim3(64 * NW), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? kOk : kEhip;
 }
 
 }  // namespace
 
 bool mla_supported(bool bf16, int kv_lora_rank, int rope_dim, int n_heads) {
-  return bf16 && kv_lora_rank == kR && rope_dim == kP && n_heads % kHeads == 0;
+  return bf16 && kv_lora_rank == kR && rope_dim == kP && n_heads % kHW == 0 &&
+         (n_heads <= kHW * kMaxWaves || n_heads % (kHW * kMaxWaves) == 0);
 }
 
-int mla_heads_per_group() { return kHeads; }
+int mla_heads_per_group(int n_heads) { return min(n_heads, kHW * kMaxWaves); }
 int mla_tile_tokens() { return kTile; }
 
 int launch_mla(const MlaParams& p, hipStream_t stream) {
-  const int n_items = p.batch * (p.n_heads / kHeads) * p.nsplit;
-  hipLaunchKernelGGL(mla_kernel, dim3(n_items), dim3(kThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return kEhip;
+  int rc = kEunsupported;
+  switch (mla_heads_per_group(p.n_heads) / kHW) {
+    case 1: rc = launch_nw<1>(p, stream); break;
+    case 2: rc = launch_nw<2>(p, stream); break;
+    case 3: rc = launch_nw<3>(p, stream); break;
+    case 4: rc = launch_nw<4>(p, stream); break;
+    default: break;
+  }
+  if (rc != kOk) return rc;
   if (p.nsplit > 1) {
-    hipLaunchKernelGGL(mla_combine, dim3(p.batch * p.n_heads), dim3(kThreads), 0, stream, p);
+    static_assert(kHW % kCombineHeads == 0, "head counts are multiples of 32");
+    hipLaunchKernelGGL(mla_combine, dim3(p.batch * p.n_heads / kCombineHeads),
+                       dim3(kCombineThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return kEhip;
   }
   return kOk;

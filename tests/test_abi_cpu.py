@@ -154,11 +154,18 @@ def test_mla_validation(L, kw, code):
 
 
 def test_mla_workspace_size(L):
-    # 32 sequences x 8 head groups already fill 256 workgroups: no split, no workspace
-    assert L.mla_decode_workspace_size(32, 128, 512, 4096) == 0
-    # one sequence: 8 head groups, context split into ceil(256 / 8) = 32 pieces of 128 tokens
-    assert L.mla_decode_workspace_size(1, 128, 512, 4096) == 1 * 32 * 128 * 514 * 4
-    assert L.mla_decode_workspace_size(1, 100, 512, 4096) == 0
+    # One workgroup serves up to 128 heads of a sequence; the context is split
+    # until about 256 workgroups run, in pieces that are whole 32-token tiles.
+    # Per piece and head: 512 bf16 (O / l) + max and sum in fp32.
+    per = 512 * 2 + 8
+    # 32 sequences x 1 head group -> 8 pieces of 512 tokens
+    assert L.mla_decode_workspace_size(32, 128, 512, 4096) == 32 * 8 * 128 * per
+    # one sequence -> 128 pieces of 32 tokens (the tile)
+    assert L.mla_decode_workspace_size(1, 128, 512, 4096) == 1 * 128 * 128 * per
+    # 256 sequences fill the GPU unsplit: no workspace
+    assert L.mla_decode_workspace_size(256, 128, 512, 4096) == 0
+    assert L.mla_decode_workspace_size(1, 100, 512, 4096) == 0   # not a multiple of 32
+    assert L.mla_decode_workspace_size(1, 160, 512, 4096) == 0   # above 128, not a multiple
 
 
 def test_binding_rejects_cpu_tensors():
