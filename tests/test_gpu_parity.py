@@ -336,6 +336,30 @@ def test_mla_split_context(lens):
     check(host(o), ref, "bf16", "MLA split")
 
 
+@pytest.mark.parametrize("n_heads,batch,lens", [
+    (32, 3, [200, 31, 97]),        # one wave per workgroup
+    (64, 2, [129, 300]),           # two waves
+    (96, 2, [64, 257]),            # three waves
+    (256, 2, [150, 33]),           # two workgroups per sequence
+    (128, 300, None),              # enough sequences to fill the GPU unsplit (no workspace)
+])
+def test_mla_head_counts(n_heads, batch, lens):
+    say(f"case: MLA n_heads={n_heads} batch={batch} lens={lens}")
+    ctx = 64 if lens is None else max(lens) + 5
+    c = inputs.mla_case(11, batch=batch, ctx=ctx, n_heads=n_heads, seq_lens=lens)
+    lat = c.latent.copy()
+    for b, L in enumerate(c.seq_lens):
+        lat[b, int(L):] = np.nan
+    maxlen = int(max(c.seq_lens))
+    o = host(pk.mla_decode_latent(dev(c.q_abs, "bf16"), dev(lat, "bf16"), i32(c.seq_lens),
+                                  kv_lora_rank=512, max_seq_len=maxlen, attention_scale=c.scale))
+    bsel = list(range(batch)) if batch <= 4 else [0, 1, batch // 2, batch - 1]
+    ref = O.mla_decode_latent(c.q_abs, c.latent, c.seq_lens, 512, c.scale, batch_indices=bsel)
+    check(o[bsel], ref, "bf16", f"MLA H={n_heads}")
+    if lens is None:
+        assert pk.mla_decode_workspace_size(batch, n_heads, 512, maxlen) == 0
+
+
 def test_mla_bad_length_gives_nan():
     say("case: MLA with an out-of-range length")
     c = inputs.mla_case(5, batch=32, ctx=256)
