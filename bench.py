@@ -149,7 +149,7 @@ def main():
                                             attention_scale=m.scale, out=mout, workspace=mws),
             bytes=ml.numel() * 2 + mq.numel() * 2 + mout.numel() * 2 + 32 * 4,
             flops=32 * 128 * 4096 * (2 * 576 + 2 * 512), bound="hbm", kind="mla",
-            kernel="mla_kernel")
+            kernel="mla_kernel + mla_combine")
         m.latent = m.q_abs = None
 
     # ---- 3. chunked prefill on paged K/V
