@@ -14,6 +14,15 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// Non-temporal store for results that a later kernel reads: the line streams
+// to memory now instead of staying dirty in the caches, where the next kernel,
+// often a bandwidth-bound decode, would pay for its write-back.
+template <typename V>
+__device__ __forceinline__ void store_nt(V* p, V v) {
+  __builtin_nontemporal_store(v, p);
+}
 
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -104,7 +104,7 @@ __device__ __forceinline__ int valid_len(const DecodeParams& p, int b) {
   return (L >= 1 && L <= p.max_seq_len) ? L : 0;
 }
 
-template <bool BF16, int D, int GMAX, bool PAGED>
+template <bool BF16, int D, int GMAX, bool PAGED, bool WIDE = false>
 __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4)) void decode_partial(DecodeParams p) {
   constexpr int E = Lane16<BF16>::E;
   constexpr int LG = D / E;          // lanes per (token, kv head) row
@@ -210,16 +210,15 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
     bool bad = false;
     const int seq_row0 = PAGED ? 0 : b * p.kv_capacity;   // first cache row of sequence b
 
-    // Sub-pieces keep the block ids they touch inside the LDS window.
-    const int span = (int)min<int64_t>(
-        PAGED ? ((int64_t)(kBtWin - 1) << shift) : (int64_t)(t_hi - t_lo), t_hi - t_lo);
-    for (int c0 = t_lo; c0 < t_hi; c0 += span) {
-      const int c1 = min(t_hi, c0 + span);
+    // Tokens [c0, c1) of the piece, with the block ids they touch in the LDS
+    // window (at most kBtWin). Returns false when a block lies outside the
+    // pool (then nothing is read).
+    auto sub_piece = [&](int c0, int c1) -> bool {
       int blk0 = 0;
       if constexpr (PAGED) {
         blk0 = c0 >> shift;
         const int nblk = ((c1 - 1) >> shift) - blk0 + 1;
-        __syncthreads();   // previous sub-piece's readers are done with s_blk
+        __syncthreads();   // previous readers are done with s_blk
         if (tid == 0) s_bad = 0;
         __syncthreads();
         for (int i = tid; i < nblk; i += kThreads) {
@@ -228,28 +227,31 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
           if (id < 0 || id >= p.num_blocks) s_bad = 1;
         }
         __syncthreads();
-        if (s_bad) { bad = true; break; }  // a block outside the pool: read nothing
+        if (s_bad) return false;
       }
 
-      // Load the K and V rows of the batch starting at token t0 into kx, vx.
-      auto load_batch = [&](uint4 (&kx)[U], uint4 (&vx)[U], int t0) {
+      // Load the K (or V) rows of the batch starting at token t0. Rows past the
+      // piece read as zero.
+      auto row_off = [&](int t) -> uint64_t {
+        // pool (or cache) row index; the host checks that it fits in 31 bits
+        const uint32_t row = PAGED ? (uint32_t)((s_blk[(t >> shift) - blk0] << shift) + (t & bs_mask))
+                                   : (uint32_t)(seq_row0 + t);
+        return (uint64_t)row * row_bytes;
+      };
+      auto load_rows = [&](uint4 (&x)[U], const char* base, int t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int t = t0 + u * R;
-          kx[u] = make_uint4(0, 0, 0, 0);
-          vx[u] = make_uint4(0, 0, 0, 0);
-          if (t < c1) {
-            // pool (or cache) row index; the host checks that it fits in 31 bits
-            const uint32_t row = PAGED ? (uint32_t)((s_blk[(t >> shift) - blk0] << shift) + (t & bs_mask))
-                                       : (uint32_t)(seq_row0 + t);
-            const uint64_t off = (uint64_t)row * row_bytes;
-            kx[u] = *(const uint4*)(kbase0 + off);
-            vx[u] = *(const uint4*)(vbase0 + off);
-          }
+          x[u] = make_uint4(0, 0, 0, 0);
+          if (t < c1) x[u] = *(const uint4*)(base + row_off(t));
         }
       };
       // Scores, online softmax and p * v for the batch at t0.
-      auto consume = [&](const uint4 (&kx)[U], const uint4 (&vx)[U], int t0) {
+      // Scores, online softmax and p * v for the batch at t0; as soon as the
+      // K (then V) rows of this batch are consumed, the registers are refilled
+      // with the next batch's rows, so a batch is always in flight.
+      auto consume = [&](uint4 (&kx)[U], uint4 (&vx)[U], int t0) {
+        const int tn = t0 + R * U;   // next batch
         float s[U][GMAX];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
 #pragma unroll
           for (int h = 0; h < GMAX; ++h) s[u][h] = group_sum<LG>(s[u][h]);
         }
+        load_rows(kx, kbase0, tn);
         // Online softmax against a reference max m: rescale only when a score
         // exceeds m by more than 2^kLazy in the exp2 domain (weights stay <= 2^kLazy).
         bool grow = false;
@@ -317,12 +320,24 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
               for (int e = 0; e < E; ++e) acc[h][e] = fmaf(s[u][h], x[e], acc[h][e]);
           }
         }
+        load_rows(vx, vbase0, tn);
       };
-      for (int t0 = c0 + r; t0 < c1; t0 += R * U) {
-        uint4 kx[U], vx[U];
-        load_batch(kx, vx, t0);
-        consume(kx, vx, t0);
+      uint4 kx[U], vx[U];
+      load_rows(kx, kbase0, c0 + r);
+      load_rows(vx, vbase0, c0 + r);
+      for (int t0 = c0 + r; t0 < c1; t0 += R * U) consume(kx, vx, t0);
+      return true;
+    };
+    if constexpr (PAGED && WIDE) {
+      // Pieces whose blocks may exceed the window: sub-pieces of kBtWin - 1 blocks.
+      const int span = (int)min<int64_t>((int64_t)(kBtWin - 1) << shift, t_hi - t_lo);
+      for (int c0 = t_lo; c0 < t_hi; c0 += span) {
+        if (!sub_piece(c0, min(t_hi, c0 + span))) { bad = true; break; }
       }
+    } else {
+      // The launcher has checked that every piece's blocks fit in the window:
+      // no loop here, which keeps the kernel's registers down.
+      bad = !sub_piece(t_lo, t_hi);
     }
 
     const int64_t slot = (int64_t)(wg + b) * p.n_heads + (int64_t)slab * HS;
@@ -371,11 +386,13 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
         if (h < G) {
           float* d = p.ws_o + (slot + kvl * G + h) * D + li * E;
 #pragma unroll
-          for (int e = 0; e < E; e += 4)
-            *(float4*)(d + e) = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+          for (int e = 0; e < E; e += 4) {
+            const f32x4_t w = {acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+            store_nt((f32x4_t*)(d + e), w);
+          }
           if (li == 0) {
-            p.ws_ml[(slot + kvl * G + h) * 2 + 0] = m[h] * c;
-            p.ws_ml[(slot + kvl * G + h) * 2 + 1] = l[h];
+            store_nt(p.ws_ml + (slot + kvl * G + h) * 2 + 0, m[h] * c);
+            store_nt(p.ws_ml + (slot + kvl * G + h) * 2 + 1, l[h]);
           }
         }
       }
@@ -386,8 +403,10 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
 
 // Merge the pieces of one sequence in range order, one thread per output:
 //   o = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w,
-// computed in one pass with a running maximum (four pieces per step so their
-// loads overlap).
+// computed with a running maximum. The loads of up to kCombineBatch pieces
+// are issued together, so a typical sequence costs one memory round trip.
+constexpr int kCombineBatch = 16;
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
   constexpr int HPW = kThreads / D > 0 ? kThreads / D : 1;  // heads per workgroup
@@ -403,10 +422,10 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
     const int cb = p.ws_cum[b];
     const int w0 = cb / per, w1 = (cb + L - 1) / per;
     float M = -INFINITY, num = 0.0f, den = 0.0f;
-    for (int w = w0; w <= w1; w += 4) {
-      float mm[4], ll[4], oo[4];
+    for (int w = w0; w <= w1; w += kCombineBatch) {
+      float mm[kCombineBatch], ll[kCombineBatch], oo[kCombineBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kCombineBatch; ++j) {
         const int64_t s = (int64_t)(w + j + b) * p.n_heads + h;
         const bool ok = w + j <= w1;
         mm[j] = ok ? p.ws_ml[s * 2] : -INFINITY;
@@ -414,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
         oo[j] = ok ? p.ws_o[s * D + d] : 0.0f;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kCombineBatch; ++j) {
         if (w + j <= w1) {
           const float Mn = fmaxf(M, mm[j]);
           const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
@@ -429,9 +448,9 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
   }
   const int64_t o = ((int64_t)b * p.n_heads + h) * D + d;
   if constexpr (BF16) {
-    ((__bf16*)p.o)[o] = (__bf16)out;
+    store_nt((__bf16*)p.o + o, (__bf16)out);
   } else {
-    ((float*)p.o)[o] = out;
+    store_nt((float*)p.o + o, out);
   }
 }
 
@@ -458,7 +477,16 @@ int launch_one(DecodeParams p, hipStream_t stream) {
   p.n_ranges = resident_ranges<BF16, D, GMAX>(p);
   if (p.n_ranges < 1) return kEhip;
   dim3 grid(p.n_ranges, p.nslab);
-  hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED>), grid, dim3(kThreads), 0, stream, p);
+  // A piece holds at most `per` tokens, per <= max(min range, ceil(B * max_len / ranges)),
+  // so it touches at most per / block_size + 2 blocks.
+  const int64_t by_len = ((int64_t)p.batch * p.max_seq_len + p.n_ranges - 1) / p.n_ranges;
+  const int64_t per_max = by_len > p.min_tokens_per_range ? by_len : p.min_tokens_per_range;
+  const bool wide = PAGED && (per_max >> p.block_shift) + 2 > kBtWin;
+  if (wide) {
+    hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED, true>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED, false>), grid, dim3(kThreads), 0, stream, p);
+  }
   if (hipGetLastError() != hipSuccess) return kEhip;
   constexpr int HPW = kThreads / D > 0 ? kThreads / D : 1;
   const int cgrid = p.batch * ((p.n_heads + HPW - 1) / HPW);

@@ -408,8 +408,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     const int64_t w = ((int64_t)b * p.nsplit + split) * p.n_heads + head;
     dst = p.ws_o + (((int64_t)b * p.nsplit + split) * p.n_heads + hg * kHW * NW) * kR;
     if (hf == 0) {
-      p.ws_ml[w * 2 + 0] = n_t > 0 ? m_ref * c : -INFINITY;
-      p.ws_ml[w * 2 + 1] = n_t > 0 ? l_tot : 0.0f;
+      store_nt(p.ws_ml + w * 2 + 0, n_t > 0 ? m_ref * c : -INFINITY);
+      store_nt(p.ws_ml + w * 2 + 1, n_t > 0 ? l_tot : 0.0f);
     }
   }
   constexpr int kOutRow = kR * 2 + 8;
@@ -430,8 +430,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   __bf16* my_dst = dst + (int64_t)(wave * kHW) * kR;
 #pragma unroll 4
   for (int r = 0; r < kHW; ++r) {
-    const uint4 v = *(const uint4*)(my_rows + r * kOutRow + 16 * lane);
-    *(uint4*)(my_dst + (int64_t)r * kR + 8 * lane) = v;
+    const u32x4_t v = *(const u32x4_t*)(my_rows + r * kOutRow + 16 * lane);
+    store_nt((u32x4_t*)(my_dst + (int64_t)r * kR + 8 * lane), v);
   }
 }
 
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine(MlaParams p) {
   const float inv = bad ? __builtin_nanf("") : 1.0f / den;
   const bf16x4_t out = {(__bf16)(num[0] * inv), (__bf16)(num[1] * inv), (__bf16)(num[2] * inv),
                         (__bf16)(num[3] * inv)};
-  *(bf16x4_t*)((__bf16*)p.o + (int64_t)bh * kR + d) = out;
+  store_nt((bf16x4_t*)((__bf16*)p.o + (int64_t)bh * kR + d), out);
 }
 
 template <int NW>

@@ -406,29 +406,49 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (; kt < n_kt && !poisoned; ++kt) poisoned = !step(kt, std::true_type{});
 
     if (!poisoned) {
-      // ---- epilogue: l = both halves' shares; O^T / l -> o[b, row, h, :]
+      // ---- epilogue: l = both halves' shares; O^T / l -> o[b, row, h, :].
+      // The tile goes through LDS so that each row leaves as whole 16-byte
+      // chunks, full lines that non-temporal stores write straight to memory.
       const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                         __float_as_uint(l_run), false, false);
       const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-      if (qrow < p.seq_q) {
-        const float inv = 1.0f / l_tot;
-        T* og = (T*)p.o + (((int64_t)b * p.seq_q + qrow) * p.n_heads + h) * D;
+      const float inv = 1.0f / l_tot;
+      constexpr int OROW = ROWB + 16;          // padded LDS row of the output tile
+      constexpr int ORP = 64 / CPR;            // rows one wave stores per pass
+      static_assert(kBlockM * OROW <= (int)sizeof(s_kv), "output tile fits in the K/V ring");
+      static_assert(32 % ORP == 0, "a wave's 32 rows split into whole passes");
+      // Every step ends on a workgroup barrier, so no wave still reads the
+      // K/V ring here and it can take the output tile.
+      char* s_out = &s_kv[0][0][0] + wave * 32 * OROW;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int d = db * 32 + 8 * g4 + 4 * hf;
-            if (d < D) {
-              if constexpr (BF16) {
-                bf16x4_t w = {(__bf16)(oacc[db][4 * g4 + 0] * inv), (__bf16)(oacc[db][4 * g4 + 1] * inv),
-                              (__bf16)(oacc[db][4 * g4 + 2] * inv), (__bf16)(oacc[db][4 * g4 + 3] * inv)};
-                *(bf16x4_t*)(og + d) = w;
-              } else {
-                *(float4*)(og + d) = make_float4(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
-                                                 oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-              }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4 + 4 * hf;
+          if (d < D) {
+            char* dst = s_out + lr * OROW + d * ESZ;
+            if constexpr (BF16) {
+              *(bf16x4_t*)dst = bf16x4_t{(__bf16)(oacc[db][4 * g4 + 0] * inv), (__bf16)(oacc[db][4 * g4 + 1] * inv),
+                                         (__bf16)(oacc[db][4 * g4 + 2] * inv), (__bf16)(oacc[db][4 * g4 + 3] * inv)};
+            } else {
+              *(f32x4_t*)dst = f32x4_t{oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv,
+                                       oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
             }
           }
+        }
+      // A wave reads back only its own rows, after its own LDS writes (LDS
+      // operations of one wave complete in order).
+      const int row0 = q0 + wave * 32;       // the wave's first query row (uniform)
+      char* og = (char*)p.o + ((((int64_t)b * p.seq_q + row0) * p.n_heads + h) * D) * ESZ;
+      const uint32_t ostride = (uint32_t)(p.n_heads * ROWB);   // bytes between query rows
+      const int rr0 = lane / CPR, cc = lane % CPR;
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += ORP) {
+        const int rr = r0 + rr0;
+        if (row0 + rr < p.seq_q) {
+          const u32x4_t v = *(const u32x4_t*)(s_out + rr * OROW + cc * 16);
+          store_nt((u32x4_t*)(og + (uint32_t)rr * ostride + cc * 16), v);
+        }
       }
       return;
     }
