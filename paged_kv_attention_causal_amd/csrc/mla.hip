@@ -88,33 +88,6 @@ __device__ __forceinline__ bf16x4_t ds_read_tr16(const char* p) {
 
 __device__ __forceinline__ int swz(int r) { return 2 * (r % 4) + (r / 4) % 2; }
 
-// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] in [15:14]; the others at their maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// One 16-byte-per-lane DMA copy global -> LDS from a uniform base plus a
-// per-lane 32-bit offset: lane i's 16 bytes land at LDS byte lds + 16 * i (M0
-// holds the wave's base; one wait state after writing it). Issued as inline assembly so the compiler does not track it: it would
-// otherwise wait for every copy in flight before each LDS read it cannot
-// prove disjoint. Completion is awaited with counted vmcnt waits.
-// The base and the LDS address are uniform by construction; passing them
-// through readfirstlane lets the compiler prove it, so they always get the
-// scalar registers the instruction needs.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"((const void*)(uintptr_t)sb), "s"(sl)
-               : "memory", "m0");
-}
-
 // acc *= alpha with acc kept in accumulation registers (read, scale and write
 // back in place; plain VALU arithmetic on them makes the compiler move all of
 // them through VGPRs on every loop trip). The s_nops cover the MFMA-write to

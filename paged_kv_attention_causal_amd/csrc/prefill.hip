@@ -6,11 +6,14 @@
 // (repeat_kv_heads). The softmax is computed online over key tiles.
 //
 // One workgroup = 4 waves = 128 query rows of one (sequence, head); each
-// wave owns 32 rows. Key tiles of 64 rows move through a two-stage LDS ring:
-// while a tile is consumed, the next one is loaded into registers and
-// written to the other stage afterwards, so there is one barrier per tile.
-// K and V stay row-major in LDS with padded rows, which keeps the operand
-// reads free of bank conflicts and their addresses immediate offsets:
+// wave owns 32 rows. Key tiles of 64 rows reach LDS by global -> LDS copies
+// (no staging registers) into two rings, K one tile ahead of V, so that one
+// step overlaps the MFMAs of the next tile's scores with the VALU softmax of
+// the current one:
+//   step t: copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T while P(t) = exp2(S(t)
+//   - m); O^T += V(t)^T P(t)^T; row max of S(t+1); one barrier.
+// The LDS image of a tile spreads rows over the banks so that the operand
+// reads are free of bank conflicts with lane-base-plus-immediate addresses:
 //   S^T = K Q^T on 32x32 MFMAs (Q^T in registers as the B operand): in the
 //     accumulator layout lane l owns query row l % 32 and 16 of each 32 keys,
 //     the other 16 sit in lane l ^ 32; the row max needs one cross-half
@@ -81,20 +84,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   constexpr int E = 16 / ESZ;                 // elements per 16-byte chunk
   constexpr int ROWB = D * ESZ;               // bytes per K/V row
   constexpr int CPR = ROWB / 16;              // chunks per row
-  // LDS row stride: 256-byte bf16 rows padded to 304 bytes (76 words, 12 banks
-  // apart): the 16 rows of a K-operand read start in 16 different bank
-  // groups and the 4 rows of a transposed V read cover disjoint banks, with
-  // every LDS address a lane base plus an immediate.
-  constexpr int LROW = BF16 ? ROWB + 48 : ROWB + 16;
-  constexpr int TILEB = kBlockN * LROW;       // LDS bytes per K (or V) tile
+  // LDS image of a key tile, filled by global -> LDS copies of 1 KB (64 lanes
+  // x 16 bytes, back to back in LDS). bf16 (256-byte rows): copy x holds rows
+  // x, x + 16, x + 32, x + 48 and sits at sigma(x) * 1040 bytes with
+  // sigma(4u + j) = 4j + u. The 16 rows of a K-operand read then start in 16
+  // different 16-byte bank groups, the 4 rows x 4 chunks of a transposed V
+  // read are disjoint, and every address is a lane base plus an immediate.
+  // fp32 (64-byte rows, the small head size): rows back to back.
   constexpr int NCH = kBlockN * CPR;          // chunks per tile
-  constexpr int LPT = (NCH + kThreads - 1) / kThreads;  // chunk loads per thread per tile
+  constexpr int kCopies = NCH / 64;           // 1 KB copies per tile
+  constexpr int kCopiesW = kCopies / 4;       // per wave
+  constexpr int TILEB = BF16 ? 15 * 1040 + 1024 : kBlockN * ROWB;
   constexpr int DB = (D + 31) / 32;           // 32-row blocks of O^T
   constexpr int KSTEPS = D / M::K;            // MFMAs per 32x32 S^T block
   static_assert(D % E == 0 && D % M::K == 0, "unsupported head size");
   static_assert(!BF16 || CPR == 16, "the bf16 path is laid out for 256-byte rows");
+  static_assert(NCH % kThreads == 0 && kCopies % 4 == 0, "every wave copies the same number of chunks");
 
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILEB];   // [stage][K|V]
+  // [0][slot] = K ring, [1][slot] = V ring. K runs one tile ahead of V.
+  __shared__ __attribute__((aligned(16))) char s_ring[2][2][TILEB];
   __shared__ int s_bt[PAGED ? kBtWin : 1];
   __shared__ int s_bad;
 
@@ -151,63 +159,43 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     }
     __syncthreads();
   };
-
-  // Global loads of key tile kt into registers (16-byte chunks). Rows past
-  // last_key are masked for every row of the tile and read as zero; tiles
-  // wholly below it load unconditionally from a uniform base and a
-  // loop-invariant per-thread offset.
-  uint4 stK[LPT], stV[LPT];
-  static_assert(NCH % kThreads == 0, "every thread loads the same number of chunks");
-  auto fetch = [&](int kt) {
-    const int k0 = kt * kBlockN;
-    if (k0 + kBlockN - 1 <= last_key) {
-#pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const int ci = tid + kThreads * j;
-        const int row = ci / CPR, cc = ci % CPR;
-        if constexpr (PAGED) {
-          const int t = k0 + row;
-          const uint32_t prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
-          const uint64_t o = (uint64_t)prow * row_bytes + (uint32_t)(cc * 16);
-          stK[j] = *(const uint4*)(kg + o);
-          stV[j] = *(const uint4*)(vg + o);
-        } else {
-          const int64_t tb = (int64_t)(seq_row0 + k0) * row_bytes;
-          const uint32_t o = (uint32_t)row * row_bytes + (uint32_t)(cc * 16);
-          stK[j] = *(const uint4*)(kg + tb + o);
-          stV[j] = *(const uint4*)(vg + tb + o);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const int ci = tid + kThreads * j;
-        const int row = ci / CPR, cc = ci % CPR;
-        const int t = k0 + row;
-        stK[j] = make_uint4(0, 0, 0, 0);
-        stV[j] = make_uint4(0, 0, 0, 0);
-        if (t <= last_key) {
-          uint32_t prow;
-          if constexpr (PAGED) {
-            prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
-          } else {
-            prow = (uint32_t)(seq_row0 + t);
-          }
-          const uint64_t o = (uint64_t)prow * row_bytes + (uint32_t)(cc * 16);
-          stK[j] = *(const uint4*)(kg + o);
-          stV[j] = *(const uint4*)(vg + o);
-        }
+  // Make sure the window holds every block of key tiles lo .. hi (lo's first
+  // block is where a reload starts). False on a bad block id.
+  auto cover = [&](int lo, int hi) -> bool {
+    if constexpr (PAGED) {
+      const int last = min(last_key, hi * kBlockN + kBlockN - 1) >> shift;
+      if (last >= win_end) {   // uniform: every thread holds the same window
+        load_window((lo * kBlockN) >> shift);
+        if (s_bad) return false;
       }
     }
+    return true;
   };
-  auto stash = [&](int stage) {
+
+  // Byte offset of copy x, and of key row r, inside a tile's LDS image.
+  auto copy_off = [](int x) -> int { return BF16 ? (4 * (x % 4) + x / 4) * 1040 : 1024 * x; };
+  auto row_off = [&](int r) -> int { return BF16 ? copy_off(r % 16) + 256 * (r / 16) : r * ROWB; };
+
+  // Copy the K (or V) rows of key tile kt into the LDS image at slot: this
+  // wave's share of the copies, 16 bytes per lane. Rows past last_key copy
+  // row last_key instead (finite data; the mask and P = 0 discard them), so
+  // every wave always issues kCopiesW copies.
+  auto issue = [&](const char* g, int kt, char* slot) {
+    const int k0 = kt * kBlockN;
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(slot);
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ci = tid + kThreads * j;
-      const int row = ci / CPR, cc = ci % CPR;
-      const int o = row * LROW + cc * 16;
-      *(uint4*)(s_kv[stage][0] + o) = stK[j];
-      *(uint4*)(s_kv[stage][1] + o) = stV[j];
+    for (int jj = 0; jj < kCopiesW; ++jj) {
+      const int x = wave + 4 * jj;
+      const int row = BF16 ? x + 16 * (lane / 16) : 16 * x + lane / CPR;
+      const int cc = lane % CPR;
+      const int t = min(k0 + row, last_key);
+      if constexpr (PAGED) {
+        const uint32_t prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
+        dma16_addr(g + (uint64_t)prow * row_bytes + cc * 16, lds + copy_off(x));
+      } else {
+        dma16(g + (int64_t)(seq_row0 + k0) * row_bytes, (uint32_t)(t - k0) * row_bytes + cc * 16,
+              lds + copy_off(x));
+      }
     }
   };
 
@@ -242,12 +230,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int wave_pos_first = off + q0 + wave * 32;
     const int my_pos = off + qrow;
     const bool wave_live = q0 + wave * 32 < p.seq_q;
+    // Tiles this wave computes (0 .. n_w - 1), and the first one that needs
+    // the mask (crosses the wave's diagonal or the end of the keys).
+    const int n_w = wave_live ? min(n_kt, (wave_pos_first + 31) / kBlockN + 1) : 0;
+    const int kt_open = min(min((wave_pos_first + 1) / kBlockN, p.seq_kv / kBlockN), n_w);
 
-    // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-    auto tile = [&](bool need_mask, int k0, int stage) {
-      const char* sK = s_kv[stage][0];
-      const char* sV = s_kv[stage][1];
-      f32x16_t s[2];
+    // S^T = K Q^T for the K tile at sK.
+    auto qk = [&](const char* sK, f32x16_t (&s)[2]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16_t acc = f32x16_t{};
@@ -256,39 +245,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         for (int kk = 0; kk < KSTEPS; ++kk) {
           typename M::Op a;
           if constexpr (BF16) {
-            a = *(const bf16x8_t*)(sK + row * LROW + (2 * kk + hf) * 16);
+            a = *(const bf16x8_t*)(sK + row_off(row) + (2 * kk + hf) * 16);
           } else {
-            a = *(const float*)(sK + row * LROW + (kk * 2 + hf) * 4);
+            a = *(const float*)(sK + row_off(row) + (kk * 2 + hf) * 4);
           }
           acc = M::mma(a, qB[kk], acc);
         }
         s[kb] = acc;
       }
-
-      // Accumulator register r of key block kb holds key k0 + 32*kb + 8*(r/4) + 4*hf + r%4.
-      if (need_mask) {
-        const int lim = min(my_pos, p.seq_kv - 1) - (k0 + 4 * hf);
+    };
+    // Accumulator register r of key block kb holds key k0 + 32*kb + 8*(r/4) + 4*hf + r%4.
+    auto mask = [&](int k0, f32x16_t (&s)[2]) {
+      const int lim = min(my_pos, p.seq_kv - 1) - (k0 + 4 * hf);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r / 4) + (r % 4) > lim) s[kb][r] = -INFINITY;
-      }
-
-      // Row max over this lane's 32 keys, then across the two lane halves.
-      // (maximum, not maxnum: no canonicalising moves; scores carry no NaN
-      // unless the inputs do, and then the row is NaN either way.)
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r / 4) + (r % 4) > lim) s[kb][r] = -INFINITY;
+    };
+    // Row max over the tile (this lane's 32 keys, then across the two lane
+    // halves); the reference max moves only when it grows by more than
+    // 2^kLazy, and then O and l are rescaled. (maximum, not maxnum: no
+    // canonicalising moves; scores carry no NaN unless the inputs do, and
+    // then the row is NaN either way.)
+    auto update_max = [&](const f32x16_t (&s)[2]) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
           mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[kb][r]), s[kb][r + 1]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                         false, false);
-        mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > kLazy) != 0) {   // wave-uniform
         const float m_new = fmaxf(m_ref, mx);
         const float alpha =
@@ -298,6 +287,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       }
+    };
+    // P = 2^((s - m_ref) c), l += row sums of P, O^T += V^T P^T.
+    auto exp_pv = [&](f32x16_t (&s)[2], const char* sV) {
       // Key 0 is visible to every row, so m_ref is finite from the first tile on.
       const float mc = m_ref == -INFINITY ? 0.0f : m_ref * c;
 #pragma unroll
@@ -308,7 +300,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           const float x = BF16 ? fmaf(sv, c, -mc) : (sv - m_ref) * c;
           s[kb][r] = __builtin_amdgcn_exp2f(x);   // masked: exp2(-inf) = 0
         }
-
       if constexpr (BF16) {
         float psum = 0.0f;
         const uint32_t ones = 0x3f803f80u;
@@ -330,8 +321,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const int chunk = 4 * db + 2 * (g16 % 2) + (i16 % 4) / 2;
-              const bf16x4_t lo = ds_read_tr16(sV + lo_row * LROW + chunk * 16 + 8 * (i16 % 2));
-              const bf16x4_t hi = ds_read_tr16(sV + hi_row * LROW + chunk * 16 + 8 * (i16 % 2));
+              const bf16x4_t lo = ds_read_tr16(sV + row_off(lo_row) + chunk * 16 + 8 * (i16 % 2));
+              const bf16x4_t hi = ds_read_tr16(sV + row_off(hi_row) + chunk * 16 + 8 * (i16 % 2));
               const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
               oacc[db] = M::mma(a, pb, oacc[db]);
             }
@@ -353,57 +344,79 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const int d = db * 32 + lr;
-              const float a = d < D ? *(const float*)(sV + key * LROW + d * 4) : 0.0f;
+              const float a = d < D ? *(const float*)(sV + row_off(key) + d * 4) : 0.0f;
               oacc[db] = M::mma(a, s[kb][r], oacc[db]);
             }
           }
       }
     };
 
-    fetch(0);
-    stash(0);
+    // ---- prologue: K0, V0 and K1 in LDS; S of tile 0.
+    issue(kg, 0, s_ring[0][0]);
+    issue(vg, 0, s_ring[1][0]);
+    if (n_kt > 1) {
+      poisoned = !cover(1, 1);
+      if (!poisoned) issue(kg, 1, s_ring[0][1]);
+    }
+    wait_vmcnt<0>();
     __syncthreads();
+    f32x16_t sc[2];   // scores of the tile being finished
+    if (!poisoned && n_w > 0) {
+      qk(s_ring[0][0], sc);
+      if (kt_open == 0) mask(0, sc);
+      update_max(sc);
+    }
+    __syncthreads();   // K slot 0 is refilled in the first step
 
-    // One step of the key loop: prefetch tile kt + 1, consume tile kt, stash
-    // the prefetch into the other stage. Returns false on a bad block id.
-    auto step = [&](int kt, auto masked_tiles) {
-      const int k0 = kt * kBlockN;
-      const int stage = kt & 1;
-      const bool more = kt + 1 < n_kt;
-      if (more) {
-        if constexpr (PAGED) {
-          const int hi = min(last_key, k0 + 2 * kBlockN - 1) >> shift;
-          if (hi >= win_end) {   // uniform: every thread holds the same window
-            load_window((k0 + kBlockN) >> shift);
-            if (s_bad) return false;
-          }
-        }
-        fetch(kt + 1);
+    // One step t: copies of K(t+2) and V(t+1) into the slots that K(t) and
+    // V(t-1) left; S(t+1) = K(t+1) Q^T on MFMA while the VALU turns S(t)
+    // into P(t); O += V(t)^T P(t)^T; row max of S(t+1). The copies land
+    // before the step's closing barrier.
+    auto step = [&](int t, auto steady) -> bool {
+      constexpr bool kSteady = decltype(steady)::value;
+      const bool more1 = kSteady || t + 1 < n_kt;
+      const bool more2 = t + 2 < n_kt;
+      if (more1) {
+        if (!cover(t + 1, more2 ? t + 2 : t + 1)) return false;
+        if (more2) issue(kg, t + 2, s_ring[0][t & 1]);
+        issue(vg, t + 1, s_ring[1][(t + 1) & 1]);
       }
-      if constexpr (decltype(masked_tiles)::value) {
-        if (wave_live && k0 <= wave_pos_first + 31) {
-          // Per wave: only tiles that cross its diagonal or the end of the keys.
-          const bool need_mask = (k0 + kBlockN - 1 > wave_pos_first) || (k0 + kBlockN > p.seq_kv);
-          tile(need_mask, k0, stage);
-        }
+      const char* sKn = s_ring[0][(t + 1) & 1];
+      const char* sV = s_ring[1][t & 1];
+      if constexpr (kSteady) {
+        f32x16_t sn[2];
+        qk(sKn, sn);
+        exp_pv(sc, sV);
+        update_max(sn);
+        sc[0] = sn[0];
+        sc[1] = sn[1];
       } else {
-        tile(false, k0, stage);
+        if (t + 1 < n_w) {
+          f32x16_t sn[2];
+          qk(sKn, sn);
+          exp_pv(sc, sV);
+          mask((t + 1) * kBlockN, sn);
+          update_max(sn);
+          sc[0] = sn[0];
+          sc[1] = sn[1];
+        } else if (t < n_w) {
+          exp_pv(sc, sV);
+        }
       }
-      if (more) stash(stage ^ 1);
+      wait_vmcnt<0>();
       __syncthreads();
       return true;
     };
 
-    // Tiles below the diagonal of the wave's first row and wholly inside the
-    // keys need no mask for any of its rows: a loop of their own without the
-    // mask code; the rest (at most two tiles) take the masking loop. Every
-    // step has the same barriers whichever loop runs it, so the switch point
-    // may differ between the waves of the workgroup.
-    const int kt_open =
-        wave_live ? min(min((wave_pos_first + 1) / kBlockN, p.seq_kv / kBlockN), n_kt) : 0;
-    int kt = 0;
-    for (; kt < kt_open && !poisoned; ++kt) poisoned = !step(kt, std::false_type{});
-    for (; kt < n_kt && !poisoned; ++kt) poisoned = !step(kt, std::true_type{});
+    // Steps whose next tile is computed by this wave without the mask take a
+    // loop of their own (no mask code, no per-step conditions on the compute
+    // side); the rest take the general loop. Every step has the same barriers
+    // whichever loop runs it, so the switch point may differ between waves.
+    int t = 0;
+    if (!poisoned) {
+      for (; t + 1 < kt_open && !poisoned; ++t) poisoned = !step(t, std::true_type{});
+      for (; t < n_kt && !poisoned; ++t) poisoned = !step(t, std::false_type{});
+    }
 
     if (!poisoned) {
       // ---- epilogue: l = both halves' shares; O^T / l -> o[b, row, h, :].
@@ -415,11 +428,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const float inv = 1.0f / l_tot;
       constexpr int OROW = ROWB + 16;          // padded LDS row of the output tile
       constexpr int ORP = 64 / CPR;            // rows one wave stores per pass
-      static_assert(kBlockM * OROW <= (int)sizeof(s_kv), "output tile fits in the K/V ring");
+      static_assert(kBlockM * OROW <= (int)sizeof(s_ring), "output tile fits in the K/V rings");
       static_assert(32 % ORP == 0, "a wave's 32 rows split into whole passes");
       // Every step ends on a workgroup barrier, so no wave still reads the
-      // K/V ring here and it can take the output tile.
-      char* s_out = &s_kv[0][0][0] + wave * 32 * OROW;
+      // rings here and they can take the output tile.
+      char* s_out = &s_ring[0][0][0] + wave * 32 * OROW;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
