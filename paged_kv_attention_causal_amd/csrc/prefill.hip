@@ -5,11 +5,14 @@
 // 0.2.4 src/attention.rs, causal_mask); query head h reads KV head h / G
 // (repeat_kv_heads). The softmax is computed online over key tiles.
 //
-// One workgroup = 4 waves = 128 query rows of one (sequence, head); each
-// wave owns 32 rows. Key tiles of 64 rows reach LDS by global -> LDS copies
-// (no staging registers) into two rings, K one tile ahead of V, so that one
-// step overlaps the MFMAs of the next tile's scores with the VALU softmax of
-// the current one:
+// One workgroup = 8 waves = 256 query rows of one (sequence, head); each
+// wave owns 32 rows, and a compute unit holds one workgroup (two waves per
+// SIMD), so that the last workgroups of a launch still keep every SIMD
+// busy with two waves, and one copy of each key tile serves 256 rows. Key
+// tiles of 64 rows reach LDS by global -> LDS copies (no staging
+// registers) into two rings, K one tile ahead of V, so that one step
+// overlaps the MFMAs of the next tile's scores with the VALU softmax of the
+// current one:
 //   step t: copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T while P(t) = exp2(S(t)
 //   - m); O^T += V(t)^T P(t)^T; row max of S(t+1); one barrier.
 // The LDS image of a tile spreads rows over the banks so that the operand
@@ -35,8 +38,9 @@ namespace pkva {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;    // keys per tile
 constexpr int kBtWin = 256;    // block-table entries cached in LDS
 constexpr int kXcds = 8;       // accelerator complex dies, each with its own L2
@@ -77,7 +81,7 @@ __device__ __forceinline__ bf16x4_t ds_read_tr16(const void* p) {
 }
 
 template <bool BF16, int D, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   using M = Mfma<BF16>;
   using T = typename M::Elem;
   constexpr int ESZ = sizeof(T);
@@ -93,16 +97,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // fp32 (64-byte rows, the small head size): rows back to back.
   constexpr int NCH = kBlockN * CPR;          // chunks per tile
   constexpr int kCopies = NCH / 64;           // 1 KB copies per tile
-  constexpr int kCopiesW = kCopies / 4;       // per wave
+  constexpr int kCopiesW = (kCopies + kWaves - 1) / kWaves;   // per wave (at most)
   constexpr int TILEB = BF16 ? 15 * 1040 + 1024 : kBlockN * ROWB;
   constexpr int DB = (D + 31) / 32;           // 32-row blocks of O^T
   constexpr int KSTEPS = D / M::K;            // MFMAs per 32x32 S^T block
   static_assert(D % E == 0 && D % M::K == 0, "unsupported head size");
   static_assert(!BF16 || CPR == 16, "the bf16 path is laid out for 256-byte rows");
-  static_assert(NCH % kThreads == 0 && kCopies % 4 == 0, "every wave copies the same number of chunks");
+  static_assert(NCH % 64 == 0, "whole copies");
+  constexpr int OROW = ROWB + 16;             // padded LDS row of the output tile
+  constexpr int LDSB = 4 * TILEB > kBlockM * OROW ? 4 * TILEB : kBlockM * OROW;
 
   // [0][slot] = K ring, [1][slot] = V ring. K runs one tile ahead of V.
-  __shared__ __attribute__((aligned(16))) char s_ring[2][2][TILEB];
+  __shared__ __attribute__((aligned(16))) char s_lds[LDSB];
+  // ring(0, slot) = K slot, ring(1, slot) = V slot. K runs one tile ahead of V.
+  auto ring = [&](int kv, int slot) -> char* { return s_lds + (kv * 2 + slot) * TILEB; };
   __shared__ int s_bt[PAGED ? kBtWin : 1];
   __shared__ int s_bad;
 
@@ -185,7 +193,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(slot);
 #pragma unroll
     for (int jj = 0; jj < kCopiesW; ++jj) {
-      const int x = wave + 4 * jj;
+      const int x = wave + kWaves * jj;
+      if (kCopies % kWaves != 0 && x >= kCopies) break;
       const int row = BF16 ? x + 16 * (lane / 16) : 16 * x + lane / CPR;
       const int cc = lane % CPR;
       const int t = min(k0 + row, last_key);
@@ -352,17 +361,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     };
 
     // ---- prologue: K0, V0 and K1 in LDS; S of tile 0.
-    issue(kg, 0, s_ring[0][0]);
-    issue(vg, 0, s_ring[1][0]);
+    issue(kg, 0, ring(0, 0));
+    issue(vg, 0, ring(1, 0));
     if (n_kt > 1) {
       poisoned = !cover(1, 1);
-      if (!poisoned) issue(kg, 1, s_ring[0][1]);
+      if (!poisoned) issue(kg, 1, ring(0, 1));
     }
     wait_vmcnt<0>();
     __syncthreads();
     f32x16_t sc[2];   // scores of the tile being finished
     if (!poisoned && n_w > 0) {
-      qk(s_ring[0][0], sc);
+      qk(ring(0, 0), sc);
       if (kt_open == 0) mask(0, sc);
       update_max(sc);
     }
@@ -378,11 +387,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       const bool more2 = t + 2 < n_kt;
       if (more1) {
         if (!cover(t + 1, more2 ? t + 2 : t + 1)) return false;
-        if (more2) issue(kg, t + 2, s_ring[0][t & 1]);
-        issue(vg, t + 1, s_ring[1][(t + 1) & 1]);
+        if (more2) issue(kg, t + 2, ring(0, t & 1));
+        issue(vg, t + 1, ring(1, (t + 1) & 1));
       }
-      const char* sKn = s_ring[0][(t + 1) & 1];
-      const char* sV = s_ring[1][t & 1];
+      const char* sKn = ring(0, (t + 1) & 1);
+      const char* sV = ring(1, t & 1);
       if constexpr (kSteady) {
         f32x16_t sn[2];
         qk(sKn, sn);
@@ -426,13 +435,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                                                         __float_as_uint(l_run), false, false);
       const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
       const float inv = 1.0f / l_tot;
-      constexpr int OROW = ROWB + 16;          // padded LDS row of the output tile
       constexpr int ORP = 64 / CPR;            // rows one wave stores per pass
-      static_assert(kBlockM * OROW <= (int)sizeof(s_ring), "output tile fits in the K/V rings");
+      static_assert(kBlockM * OROW <= LDSB, "output tile fits in the LDS block");
       static_assert(32 % ORP == 0, "a wave's 32 rows split into whole passes");
       // Every step ends on a workgroup barrier, so no wave still reads the
       // rings here and they can take the output tile.
-      char* s_out = &s_ring[0][0][0] + wave * 32 * OROW;
+      char* s_out = &s_lds[0] + wave * 32 * OROW;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
