@@ -130,7 +130,8 @@ size_t attn_decode_workspace_size(int batch, int n_heads, int n_kv_heads, int he
  *            Requires 1 <= max_seq_len <= kv_capacity.
  *   workspace: device memory of at least attn_decode_workspace_size(...)
  *            bytes, contents irrelevant on entry, clobbered on return.
- *   Built: (PKVA_F32, 16), (PKVA_BF16, 128), with n_heads / n_kv_heads <= 16.
+ *   Built: (PKVA_F32, 16), (PKVA_BF16, 128), with n_heads / n_kv_heads <= 8;
+ *            a larger group returns PKVA_EUNSUPPORTED.
  */
 int attn_decode_contig(int dtype, const void* q, const void* k_cache, const void* v_cache,
                        void* o, int batch, int n_heads, int n_kv_heads, int head_dim,

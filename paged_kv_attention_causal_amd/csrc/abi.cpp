@@ -37,6 +37,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool scale_ok(float s) { return std::isfinite(s) && s >= 0.0f; }
 
+// The softmax multiplier the kernels use: exp2((s - m) * c) with
+// c = attention_scale * log2(e). Every kernel masks a score by making it
+// -inf and starts its running max at -inf, which needs c > 0 (-inf * 0 is
+// NaN). A zero scale makes every visible score 0, i.e. uniform weights; the
+// smallest normal float gives the same weights, exp2 of a product that
+// small being exactly 1.
+float scale_log2(float attention_scale) {
+  return std::max(attention_scale * pkva::kLog2eHost, FLT_MIN);
+}
+
 bool heads_ok(int n_heads, int n_kv_heads, int head_dim) {
   return n_heads >= 1 && n_kv_heads >= 1 && head_dim >= 1 && n_heads % n_kv_heads == 0;
 }
@@ -137,8 +147,10 @@ int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o
   if (paged) {
     if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
     if ((int64_t)max_blocks_per_seq * block_size < seq_kv) return PKVA_EINVAL;
+    if ((int64_t)num_blocks * block_size > INT_MAX) return PKVA_EINVAL;   // pool rows index in 31 bits
   } else {
     if (kv_capacity < seq_kv) return PKVA_EINVAL;
+    if ((int64_t)batch * kv_capacity > INT_MAX) return PKVA_EINVAL;       // cache rows index in 31 bits
   }
   const bool bf16 = dtype == PKVA_BF16;
   if (!pkva::prefill_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
@@ -156,11 +168,7 @@ int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o
   p.num_blocks = paged ? num_blocks : 0;
   p.kv_capacity = paged ? 0 : kv_capacity;
   p.q_tiles = (int)q_tiles;
-  // The kernel masks a score by making it -inf and relies on exp2(-inf * c) = 0,
-  // which needs c > 0. A zero scale makes every visible score 0 (uniform
-  // weights); the smallest normal float gives the same weights, exp2 of a
-  // product that small being exactly 1.
-  p.scale_log2 = std::max(attention_scale * pkva::kLog2eHost, FLT_MIN);
+  p.scale_log2 = scale_log2(attention_scale);
   const int rc = pkva::launch_prefill(bf16, paged, head_dim, p, (hipStream_t)stream);
   return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
 }
@@ -215,7 +223,7 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
   p.block_shift = paged ? log2i(block_size) : 0;
   p.num_blocks = paged ? num_blocks : 0;
   p.kv_capacity = paged ? 0 : kv_capacity;
-  p.scale_log2 = attention_scale * pkva::kLog2eHost;
+  p.scale_log2 = scale_log2(attention_scale);
   const int rc = pkva::launch_decode(bf16, paged, head_dim, sh.gmax, p, (hipStream_t)stream);
   return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
 }
@@ -274,7 +282,7 @@ int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_
                             : nullptr;
   p.batch = batch; p.n_heads = n_heads; p.kv_capacity = kv_capacity; p.max_seq_len = max_seq_len;
   p.nsplit = sh.nsplit; p.split_tokens = sh.split_tokens;
-  p.scale_log2 = attention_scale * pkva::kLog2eHost;
+  p.scale_log2 = scale_log2(attention_scale);
   const int rc = pkva::launch_mla(p, (hipStream_t)stream);
   return rc == pkva::kOk ? PKVA_OK : PKVA_EHIP;
 }

@@ -34,10 +34,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One 16-byte-per-lane DMA copy global -> LDS from a uniform base plus a
-// per-lane 32-bit offset: lane i's 16 bytes land at LDS byte lds + 16 * i (M0
-// holds the wave's base; one wait state after writing it). Issued as inline assembly so the compiler does not track it: it would
+// per-lane 32-bit offset: lane i's 16 bytes land at LDS byte lds + 16 * i.
+// Issued as inline assembly so the compiler does not track it: it would
 // otherwise wait for every copy in flight before each LDS read it cannot
 // prove disjoint. Completion is awaited with counted vmcnt waits.
+// The instruction takes the wave's LDS base in M0, a register the compiler
+// reserves: the statement saves M0 in a scratch SGPR, sets it (one wait
+// state before the copy reads it), and puts the saved value back (one wait
+// state before anything after the statement may read it), so the compiler's
+// own view of M0 stays true.
 // The base and the LDS address are uniform by construction; passing them
 // through readfirstlane lets the compiler prove it, so they always get the
 // scalar registers the instruction needs.
@@ -46,20 +51,34 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"((const void*)(uintptr_t)sb), "s"(sl)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(off), "s"((const void*)(uintptr_t)sb), "s"(sl)
+      : "memory");
 }
 
 // The same copy from a per-lane 64-bit address (rows gathered from anywhere
 // in a pool that may exceed 4 GiB).
 __device__ __forceinline__ void dma16_addr(const void* addr, uint32_t lds) {
   const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(addr), "s"(sl)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(addr), "s"(sl)
+      : "memory");
 }
 
 // ---------------------------------------------------------------- bf16 bits

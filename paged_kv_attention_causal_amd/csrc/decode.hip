@@ -329,8 +329,13 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
       return true;
     };
     if constexpr (PAGED && WIDE) {
-      // Pieces whose blocks may exceed the window: sub-pieces of kBtWin - 1 blocks.
-      const int span = (int)min<int64_t>((int64_t)(kBtWin - 1) << shift, t_hi - t_lo);
+      // Pieces whose blocks may exceed the window: sub-pieces of at most
+      // kBtWin - 1 blocks (at most kBtWin block ids once misaligned). The span
+      // is a multiple of R * U tokens, so every stream takes the same tokens
+      // in the same batches as in one pass over the piece: the arithmetic,
+      // and the result, match the contiguous kernel bit for bit.
+      // (R * U is a power of two no larger than 128 <= (kBtWin - 1) << shift.)
+      const int span = ((kBtWin - 1) << shift) & ~(R * U - 1);
       for (int c0 = t_lo; c0 < t_hi; c0 += span) {
         if (!sub_piece(c0, min(t_hi, c0 + span))) { bad = true; break; }
       }

@@ -172,22 +172,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
       }
     }
   };
-  // publish(i) runs when the tiles up to min(i + kPrefetch - 1, n_t - 1) are
+  // publish(i) runs when the tiles up to min(i + kPrefetch - 2, n_t - 1) are
   // issued: wait until at most the later tiles' copies are in flight (vmcnt
-  // counts in issue order), then the barrier publishes tile i to every wave
-  // and retires every read of the stage the next copy reuses.
+  // counts in issue order), then the barrier publishes tile i to every wave.
+  // The same barrier retires every read of the stage the next copy reuses:
+  // a wave reads tile j's stage in steps j - 1 (its keys) and j (its
+  // values), and the copy of tile j + 4 into that stage is issued only after
+  // publish(j + 2), which no wave passes before it has finished step j.
   auto publish = [&](int i) {
-    const int later = max(0, min(i + kPrefetch - 1, n_t - 1) - i);
-    static_assert(kPrefetch - 1 <= 2, "extend the wait cases");
+    const int later = max(0, min(i + kPrefetch - 2, n_t - 1) - i);
+    static_assert(kPrefetch - 2 <= 1, "extend the wait cases");
     // (vmcnt holds at most 63: waiting for fewer in flight is also correct.)
     constexpr int kOne = kDmaPerThread < 63 ? kDmaPerThread : 63;
-    constexpr int kTwo = 2 * kDmaPerThread < 63 ? 2 * kDmaPerThread : 63;
     if (later == 0) {
       wait_vmcnt<0>();
-    } else if (later == 1) {
-      wait_vmcnt<kOne>();
     } else {
-      wait_vmcnt<kTwo>();
+      wait_vmcnt<kOne>();
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("" ::: "memory");
@@ -347,14 +347,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     f32x16_t sc;
     scores_and_values(sc, 0, 0, std::false_type{});
 
-    // Step i: copy tile i + kPrefetch; softmax of tile i; publish tile i + 1;
-    // its scores together with the values of tile i. The last tile is peeled
-    // off (no next tile), so the loop has no branch that would make the
-    // compiler copy O^T between register sets.
+    // Step i: softmax of tile i; publish tile i + 1; copy tile i + kPrefetch
+    // into the stage tile i - 1 left (every wave is past step i - 1 once
+    // the barrier opens); scores of tile i + 1 together with the values of
+    // tile i. The last tile is peeled off (no next tile), so the loop has no
+    // branch that would make the compiler copy O^T between register sets.
+    static_assert(kPrefetch == kStages - 1, "the copy reuses the stage of tile i - 1");
     for (int i = 0; i + 1 < n_t; ++i) {
-      if (i + kPrefetch < n_t) issue(i + kPrefetch);
       softmax(sc, i);
       publish(i + 1);
+      if (i + kPrefetch < n_t) issue(i + kPrefetch);
       scores_and_values(sc, (i + 1) % kStages, i % kStages, std::true_type{});
     }
     softmax(sc, n_t - 1);

@@ -61,6 +61,9 @@ def _prefill(L, **kw):
     (dict(bt=P, maxb=3, bs=16, nb=10), EINVAL),   # table too short for seq_kv
     (dict(bt=P, maxb=4, bs=16, nb=0), EINVAL),
     (dict(head_dim=64), EUNSUP),           # not built
+    # cache and pool rows are indexed in 31 bits
+    (dict(batch=2, cap=(1 << 30) + 1, seq_kv=64), EINVAL),
+    (dict(bt=P, maxb=4, bs=16, nb=(1 << 27)), EINVAL),
     (dict(dtype=0, head_dim=128), EUNSUP),
     (dict(dtype=1, head_dim=16), EUNSUP),
 ])

@@ -173,7 +173,10 @@ def test_prefill_full_size_sampled_rows(prefill_full):
     torch.cuda.synchronize()
     assert torch.equal(o, o2), "prefill is not deterministic"
     rng = np.random.default_rng(1)
-    rows = sorted(set([0, 1, 31, 32, 63, 64, 127, 128, 129, 2047, 2048, 4000, 4094, 4095]
+    # the first and last row of every 256-row query tile (each tile and head is
+    # its own work item), the rows around the first key tiles, and a random draw
+    edges = [r for t in range(16) for r in (256 * t, 256 * t + 255)]
+    rows = sorted(set(edges + [1, 31, 32, 63, 64, 127, 128, 129, 4000, 4094]
                       + rng.integers(0, 4096, 18).tolist()))
     ref = O.prefill(c.q, c.k, c.v, 28, 4, c.seq_kv, 0, c.scale, rows=rows)
     check(host(o)[:, rows], ref, "bf16", "prefill 4096 sampled rows")
@@ -188,7 +191,7 @@ def test_chunked_paged_prefill_full_size_sampled_rows():
     oh = host(o)
     rng = np.random.default_rng(2)
     rows = sorted(set([0, 1, 127, 128, 255, 256, 511] + rng.integers(0, 512, 6).tolist()))
-    for b in (0, 3, 7):
+    for b in range(c.batch):
         ref = O.prefill(c.q[b:b + 1], c.k, c.v, 32, 8, c.seq_kv, c.position_offset, c.scale,
                         block_table=c.block_table[b:b + 1], block_size=16, rows=rows)
         check(oh[b:b + 1, rows], ref, "bf16", f"seq {b}")
@@ -286,6 +289,56 @@ def test_decode_edge_lengths(dtype, D, H, Hkv, bs):
         assert np.array_equal(oh[0, h], vc[0, 0, h // (H // Hkv)].astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 16)])
+def test_decode_zero_scale_is_the_mean_of_the_visible_values(dtype, D):
+    lens = [1, 70, 513, 1000]
+    say(f"case: decode at attention_scale 0, dtype={dtype}, lens={lens}")
+    c = inputs.paged_decode_case(13, dtype=dtype, batch=len(lens), n_heads=8, n_kv_heads=2,
+                                 head_dim=D, block_size=16, seq_lens=lens, len_hi=1024, scale=0.0)
+    o = _run_paged(c)
+    ref = O.decode_paged(c.q, c.k_pool, c.v_pool, c.block_table, 16, c.seq_lens, 8, 2, 0.0)
+    # the oracle at scale 0 is the plain mean of the visible V rows
+    kc, vc = c.contig(capacity=1024, fill=np.nan)
+    for b, L in enumerate(lens):
+        mean = vc[b, :L].astype(np.float64).mean(axis=0)          # [Hkv, D]
+        assert np.allclose(ref[b], np.repeat(mean, 4, axis=0), atol=1e-12)
+    check(host(o), ref, dtype, "paged, scale 0")
+    oc = pk.attn_decode_contig(dev(c.q, dtype), dev(kc, dtype), dev(vc, dtype), i32(c.seq_lens),
+                               max_seq_len=1024, attention_scale=0.0)
+    assert torch.equal(oc, o), "contiguous != paged (bitwise) at scale 0"
+
+
+@pytest.mark.parametrize("H,bs,B,lo,maxlen", [(4, 1, 256, 3000, 8192), (8, 2, 512, 1000, 8200)])
+def test_paged_decode_wide_block_windows(H, bs, B, lo, maxlen):
+    """Pieces longer than the 1023-block LDS window (tiny blocks, long contexts):
+    the kernel walks sub-pieces; it must match the oracle and stay bitwise equal to
+    the contiguous kernel, which takes each piece in one pass."""
+    say(f"case: paged decode with sub-pieces, B={B} H={H} Hkv=1 bs={bs} lens U[{lo},{maxlen}]")
+    c = inputs.paged_decode_case(17, batch=B, len_lo=lo, len_hi=maxlen, n_heads=H,
+                                 n_kv_heads=1, head_dim=128, block_size=bs)
+    # the launcher takes the sub-piece kernel whenever B * max_seq_len / ranges
+    # needs more than 1022 block ids, and at most 2048 ranges are cut
+    assert B * maxlen // bs > 1022 * 2048
+    kp, vp = dev(c.k_pool, "bf16"), dev(c.v_pool, "bf16")
+    bt, lens = i32(c.block_table), i32(c.seq_lens)
+    o = _run_paged(c, kp, vp, bt, lens)
+    sel = [0, 1, 77, 128, 200, B - 1]
+    ref = O.decode_paged(c.q, c.k_pool, c.v_pool, c.block_table, bs, c.seq_lens, H, 1, c.scale,
+                         batch_indices=sel)
+    check(host(o)[sel], ref, "bf16", f"sequences {sel}")
+    kc = torch.full((B, maxlen, 1, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    btl = bt.long()
+    for b in range(B):
+        L = int(c.seq_lens[b])
+        nb = (L + bs - 1) // bs
+        kc[b, :L] = kp[btl[b, :nb]].reshape(nb * bs, 1, 128)[:L]
+        vc[b, :L] = vp[btl[b, :nb]].reshape(nb * bs, 1, 128)[:L]
+    oc = pk.attn_decode_contig(dev(c.q, "bf16"), kc, vc, lens, max_seq_len=maxlen,
+                               attention_scale=c.scale)
+    assert torch.equal(oc, o), "contiguous != paged (bitwise) with sub-pieces"
+
+
 def test_decode_bad_entries_give_nan_only_there():
     say("case: decode with a zero length and an out-of-pool block id")
     c = inputs.paged_decode_case(8, batch=5, len_lo=100, len_hi=600, n_heads=8, n_kv_heads=2)
@@ -358,6 +411,22 @@ def test_mla_head_counts(n_heads, batch, lens):
     check(o[bsel], ref, "bf16", f"MLA H={n_heads}")
     if lens is None:
         assert pk.mla_decode_workspace_size(batch, n_heads, 512, maxlen) == 0
+
+
+def test_mla_zero_scale_is_the_mean_of_the_visible_values():
+    lens = [1, 33, 700, 1500]
+    say(f"case: MLA at attention_scale 0, lens={lens}")
+    c = inputs.mla_case(9, batch=len(lens), ctx=1504, seq_lens=lens, n_heads=32)
+    lat = c.latent.copy()
+    for b, L in enumerate(lens):
+        lat[b, L:] = np.nan
+    o = pk.mla_decode_latent(dev(c.q_abs, "bf16"), dev(lat, "bf16"), i32(lens),
+                             kv_lora_rank=512, max_seq_len=max(lens), attention_scale=0.0)
+    ref = O.mla_decode_latent(c.q_abs, c.latent, lens, 512, 0.0)
+    for b, L in enumerate(lens):
+        mean = c.latent[b, :L, :512].astype(np.float64).mean(axis=0)
+        assert np.allclose(ref[b], mean[None, :], atol=1e-12)
+    check(host(o), ref, "bf16", "MLA scale 0")
 
 
 def test_mla_bad_length_gives_nan():
