@@ -27,6 +27,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <atomic>
+
 namespace pkva {
 
 namespace {
@@ -459,6 +461,19 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
   }
 }
 
+// Per-device facts the launcher needs on every call, looked up once per
+// device (compute units, and the resident workgroups per unit of each
+// kernel instantiation): the runtime queries cost microseconds per call.
+constexpr int kMaxDevices = 64;
+constexpr int kVariants = 8;    // (bf16 D=128, fp32 D=16) x group sizes 1, 2, 4, 8
+std::atomic<int> g_slots_per_cu[kMaxDevices][kVariants];   // 0 = not looked up yet
+std::atomic<int> g_cus[kMaxDevices];
+
+template <bool BF16, int GMAX>
+constexpr int variant_index() {
+  return (BF16 ? 0 : 4) + (GMAX == 1 ? 0 : GMAX == 2 ? 1 : GMAX == 4 ? 2 : 3);
+}
+
 // Token ranges for one launch: one per workgroup slot the device can keep
 // resident (compute units x workgroups per unit), never more than the
 // workspace holds or than min-size ranges the batch can fill. The slot count
@@ -466,14 +481,24 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
 // entry points always cut the same ranges and stay bitwise equal.
 template <bool BF16, int D, int GMAX>
 int resident_ranges(const DecodeParams& p) {
-  int dev = 0, cus = 0, occ_c = 0, occ_p = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_c, decode_partial<BF16, D, GMAX, false>,
-                                                   kThreads, 0) != hipSuccess) return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, decode_partial<BF16, D, GMAX, true>,
-                                                   kThreads, 0) != hipSuccess) return -1;
-  const int slots = cus * max(1, min(occ_c, occ_p)) / p.nslab;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  constexpr int vi = variant_index<BF16, GMAX>();
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  int occ = g_slots_per_cu[dev][vi].load(std::memory_order_relaxed);
+  if (cus <= 0 || occ <= 0) {
+    int occ_c = 0, occ_p = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_c, decode_partial<BF16, D, GMAX, false>,
+                                                     kThreads, 0) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, decode_partial<BF16, D, GMAX, true>,
+                                                     kThreads, 0) != hipSuccess) return -1;
+    occ = max(1, min(occ_c, occ_p));
+    // Two threads may both look it up; they store the same values.
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+    g_slots_per_cu[dev][vi].store(occ, std::memory_order_relaxed);
+  }
+  const int slots = cus * occ / p.nslab;
   return max(1, min(p.n_ranges, slots));
 }
 
