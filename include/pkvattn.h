@@ -38,6 +38,8 @@
  *                        not built (see each entry point)
  *      PKVA_EWORKSPACE   workspace NULL or smaller than the *_workspace_size call
  *      PKVA_EHIP         the kernel launch failed
+ *      PKVA_ESCRATCH     (attn_decode_paged_noalloc only) the sizes need more
+ *                        than the library's fixed scratch array holds
  *  - Device-side data errors never cause an out-of-bounds access: a sequence
  *    whose seq_lens entry is outside [1, max_seq_len], or whose block table
  *    names a block outside [0, num_blocks) among the blocks it needs, gets
@@ -48,8 +50,10 @@
  *    bitwise-identical outputs for the same cache rows (frink-models 0.38.0
  *    src/decoder/attn_block.rs, doc of push_and_attend_row: paging changes
  *    where rows live and nothing else).
- *  - The library holds no mutable global state; calls are thread-safe.
- *    Calls that share a workspace must be ordered on one stream.
+ *  - The library's only global state is a per-device cache of launch facts
+ *    (compute units, resident workgroups) and the scratch array of
+ *    attn_decode_paged_noalloc; calls are thread-safe. Calls that share a
+ *    workspace must be ordered on one stream.
  */
 #ifndef PKVATTN_H
 #define PKVATTN_H
@@ -68,7 +72,8 @@ enum {
   PKVA_EINVAL = 1,
   PKVA_EUNSUPPORTED = 2,
   PKVA_EWORKSPACE = 3,
-  PKVA_EHIP = 4
+  PKVA_EHIP = 4,
+  PKVA_ESCRATCH = 5
 };
 
 /* A static, human-readable name for a return code ("unknown status" otherwise). */
@@ -163,6 +168,29 @@ int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* 
                       int num_blocks, const int32_t* seq_lens, int max_seq_len,
                       float attention_scale, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * attn_decode_paged_noalloc: attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, layouts, validation and
+ * results (bitwise) as attn_decode_paged, without the workspace arguments:
+ * the split partials live in a fixed device array inside the library
+ * (64 MiB, one copy per device that runs the library, held until the
+ * process ends). The call allocates nothing. It needs
+ * attn_decode_workspace_size(batch, n_heads, n_kv_heads, head_dim,
+ * max_seq_len) <= 64 MiB (e.g. the 64-sequence, 32-head, D=128, 8192-token
+ * workload takes 35 MB) and returns PKVA_ESCRATCH otherwise. Every call on a
+ * device shares that device's array: calls that overlap on one device (two
+ * streams, two threads) race and must be ordered by the caller. The first
+ * call on a device looks up the array's device address (a HIP call that
+ * enqueues nothing); the call uses the current device, which must be the
+ * device of `stream`.
+ */
+int attn_decode_paged_noalloc(int dtype, const void* q, const void* k_pool, const void* v_pool,
+                              void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                              const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                              int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                              float attention_scale, void* stream);
 
 /*
  * Bytes of device workspace mla_decode_latent needs. Returns 0 for invalid sizes.

@@ -25,6 +25,7 @@ __all__ = [
     "attn_prefill",
     "attn_decode_contig",
     "attn_decode_paged",
+    "attn_decode_paged_noalloc",
     "attn_decode_workspace_size",
     "mla_decode_latent",
     "mla_decode_workspace_size",
@@ -78,6 +79,9 @@ def lib():
         L.attn_decode_paged.restype = i32
         L.attn_decode_paged.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, i32,
                                         vp, i32, f32, vp, sz, vp]
+        L.attn_decode_paged_noalloc.restype = i32
+        L.attn_decode_paged_noalloc.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
+                                                i32, i32, vp, i32, f32, vp]
         L.mla_decode_workspace_size.restype = sz
         L.mla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mla_decode_latent.restype = i32
@@ -227,6 +231,27 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, max_seq_len: 
                                  _ptr(seq_lens), max_seq_len, attention_scale, _ptr(workspace),
                                  workspace.numel(), _stream(q, stream))
     _check("attn_decode_paged", st)
+    return out
+
+
+def attn_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, *, max_seq_len: int,
+                              attention_scale: float, out, stream=None):
+    """:func:`attn_decode_paged` on the library's static scratch: allocates nothing.
+
+    ``out`` must be given (``[B, H, D]``, the dtype of ``q``). Calls that overlap
+    on one device share the scratch and must be ordered by the caller.
+    """
+    for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"), (out, "out")):
+        _dev(t, n)
+    _i32(block_table, "block_table")
+    _i32(seq_lens, "seq_lens")
+    B, H, D = q.shape
+    nb, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    st = lib().attn_decode_paged_noalloc(_dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                         _ptr(out), B, H, Hkv, D, _ptr(block_table),
+                                         block_table.shape[1], bs, nb, _ptr(seq_lens), max_seq_len,
+                                         attention_scale, _stream(q, stream))
+    _check("attn_decode_paged_noalloc", st)
     return out
 
 

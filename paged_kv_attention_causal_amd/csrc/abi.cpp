@@ -126,6 +126,7 @@ const char* pkva_status_string(int status) {
     case PKVA_EUNSUPPORTED: return "unsupported dtype or size";
     case PKVA_EWORKSPACE: return "workspace missing or too small";
     case PKVA_EHIP: return "HIP launch failed";
+    case PKVA_ESCRATCH: return "sizes exceed the static scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -184,7 +185,7 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
                          const int32_t* block_table, int max_blocks_per_seq, int block_size,
                          int num_blocks, const int32_t* seq_lens, int kv_capacity,
                          int max_seq_len, float attention_scale, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, bool use_scratch = false) {
   if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
   if (!q || !k || !v || !o || !seq_lens) return PKVA_EINVAL;
   if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim) || max_seq_len < 1) return PKVA_EINVAL;
@@ -203,6 +204,13 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
   DecodeShape sh;
   const int rc0 = decode_shape(dtype, batch, n_heads, n_kv_heads, head_dim, max_seq_len, &sh);
   if (rc0 != PKVA_OK) return rc0;
+  if (use_scratch) {
+    // Only now a HIP call (the symbol lookup, once per device); it enqueues nothing.
+    if (sh.ws_bytes > pkva::decode_scratch_bytes()) return PKVA_ESCRATCH;
+    workspace = pkva::decode_scratch();
+    workspace_bytes = pkva::decode_scratch_bytes();
+    if (!workspace) return PKVA_EHIP;
+  }
   if (!workspace || workspace_bytes < sh.ws_bytes) return PKVA_EWORKSPACE;
   if (((uintptr_t)workspace & 15u) != 0) return PKVA_EWORKSPACE;
 
@@ -247,6 +255,16 @@ int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* 
   return decode_common(dtype, true, q, k_pool, v_pool, o, batch, n_heads, n_kv_heads, head_dim,
                        block_table, max_blocks_per_seq, block_size, num_blocks, seq_lens, 0,
                        max_seq_len, attention_scale, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged_noalloc(int dtype, const void* q, const void* k_pool, const void* v_pool,
+                              void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                              const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                              int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                              float attention_scale, void* stream) {
+  return decode_common(dtype, true, q, k_pool, v_pool, o, batch, n_heads, n_kv_heads, head_dim,
+                       block_table, max_blocks_per_seq, block_size, num_blocks, seq_lens, 0,
+                       max_seq_len, attention_scale, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {

@@ -28,6 +28,7 @@
 #include "kernels.hpp"
 
 #include <atomic>
+#include <mutex>
 
 namespace pkva {
 
@@ -537,6 +538,39 @@ int launch_g(const DecodeParams& p, int gmax, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ---- scratch of attn_decode_paged_noalloc
+// The split partials, maxima, sums and prefix sums of one call, in the layout
+// of the caller-provided workspace, in a fixed device array: each device
+// that runs the library holds its own copy until the process ends. Calls
+// that overlap on one device share it and race; nothing in it has to start
+// at zero (every slot a call reads was written earlier in the same call).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of each device's copy
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+// The current device's address of the scratch array, looked up once per
+// device with that device current (the array's name in host code is only a
+// stand-in for the symbol, never a device address). Null on failure.
+void* decode_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch[dev].load(std::memory_order_relaxed);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
 
 int decode_max_ranges() { return 2048; }          // 256 CUs x 8 resident workgroups
 int decode_min_tokens_per_range() { return 64; }

@@ -41,6 +41,10 @@ bool decode_supported(bool bf16, int head_dim);
 int decode_lanes_per_row(bool bf16, int head_dim);
 int launch_decode(bool bf16, bool paged, int head_dim, int gmax, const DecodeParams& p,
                   hipStream_t stream);
+// The static scratch array of the allocation-free decode: its size, and the
+// current device's address of it (null if the lookup fails).
+size_t decode_scratch_bytes();
+void* decode_scratch();
 
 struct PrefillParams {
   const void* q;              // [batch, seq_q, n_heads, D]
