@@ -49,6 +49,9 @@ __all__ = [
     "mla_decode_latent",
     "mla_naive",
     "mla_absorbed",
+    "rope_interleaved",
+    "append_rows",
+    "mla_append_latent",
 ]
 
 
@@ -249,3 +252,77 @@ def mla_absorbed(q, c, k_rot, w_uk, w_uv, scale):
     latent = np.concatenate([c, k_rot], axis=1)
     o_lat = mla_decode_latent(q_abs[None], latent[None], [c.shape[0]], R, scale)[0]
     return np.einsum("hvr,hr->hv", w_uv, o_lat)
+
+
+# ------------------------------------------------------------------ cache append (push)
+
+def rope_interleaved(x, position, theta: float) -> np.ndarray:
+    """Interleaved rotary embedding of the last axis of ``x`` at ``position``, in float64.
+
+    The last axis (width ``d``, even) holds pairs ``(x[2i], x[2i+1])``; pair
+    ``i`` turns by the angle ``position * theta ** (-2i / d)``:
+    ``(a, b) -> (a cos - b sin, a sin + b cos)``. This is the rotation
+    frink-models 0.31.0 ``src/mla/mod.rs`` applies to the shared ``k_rot``
+    slice (module doc point 2, "interleaved convention"; ``rotate_pe`` with no
+    YaRN factors). ``position`` broadcasts against ``x.shape[:-1]``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("rotary width must be even")
+    out = np.empty_like(x)
+    pos = np.asarray(position, dtype=np.float64)
+    for i in range(d // 2):
+        angle = pos * float(theta) ** (-2.0 * i / d)
+        c, s = np.cos(angle), np.sin(angle)
+        a, b = x[..., 2 * i], x[..., 2 * i + 1]
+        out[..., 2 * i] = a * c - b * s
+        out[..., 2 * i + 1] = a * s + b * c
+    return out
+
+
+def append_rows(cache, new_rows, positions, block_table=None, block_size=0):
+    """Push ``n_new`` rows per sequence into a KV cache; returns the updated copy.
+
+    ``new_rows`` is ``[B, n_new, ...]``; row ``i`` of sequence ``b`` becomes
+    token ``t = positions[b] + i`` of that sequence (``positions[b]`` = rows it
+    held before the push). Contiguous (``block_table is None``): ``cache`` is
+    ``[B, capacity, ...]`` and the row lands at ``cache[b, t]``. Paged:
+    ``cache`` is a pool ``[num_blocks, block_size, ...]`` and the row lands at
+    ``pool[block_table[b][t // block_size]][t % block_size]``. Push-then-attend:
+    frink-models 0.38.0 ``src/decoder/attn_block.rs`` (``push_and_attend_row``
+    writes this row to whichever backing, then attends); kopitiam-runtime 0.2.4
+    ``src/attention.rs`` (``attention_forward`` appends before scoring).
+    """
+    out = np.array(cache, copy=True)
+    B, n_new = new_rows.shape[0], new_rows.shape[1]
+    for b in range(B):
+        for i in range(n_new):
+            t = int(positions[b]) + i
+            if block_table is None:
+                out[b, t] = new_rows[b, i]
+            else:
+                out[int(block_table[b][t // block_size]), t % block_size] = new_rows[b, i]
+    return out
+
+
+def mla_append_latent(latent, c_new, k_rot_new, positions, theta, block_table=None,
+                      block_size=0):
+    """Push one latent row ``[c | rope(k_rot)]`` per sequence; returns the updated float64 copy.
+
+    ``c_new`` is ``[B, R]`` (the normed compressed KV), ``k_rot_new`` is
+    ``[B, P]`` before rotation; the row written at token ``positions[b]`` is
+    ``c_new[b]`` followed by ``k_rot_new[b]`` turned by :func:`rope_interleaved`
+    at that position, once, for every head to share. ``theta <= 0`` means no
+    rotation (the rope-free configuration). frink-models 0.31.0
+    ``src/mla/mod.rs``: ``mla_forward_token`` (``k_rot`` rotated once before
+    broadcasting) and ``absorbed_attention`` (``k_cache`` extended by ``c``
+    then ``k_rot``). Layout as :func:`append_rows` with one row per sequence.
+    """
+    c_new = np.asarray(c_new, dtype=np.float64)
+    k_rot = np.asarray(k_rot_new, dtype=np.float64)
+    if theta > 0:
+        k_rot = rope_interleaved(k_rot, np.asarray(positions, dtype=np.float64), theta)
+    rows = np.concatenate([c_new, k_rot], axis=-1)[:, None, :]
+    return append_rows(np.asarray(latent, dtype=np.float64), rows, positions, block_table,
+                       block_size)

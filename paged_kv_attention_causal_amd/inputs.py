@@ -1,9 +1,8 @@
 """Seeded synthetic inputs for the attention workloads.
 
-This module draws random numbers, rounds them to the storage dtype, lays out
-block tables and pools, and rotates the ``k_rot`` slice of an MLA latent row
-(the latent cache stores that slice already rotated). It computes no
-attention: no scores, no softmax, no weighted sums. Both the oracle side and
+This module draws random numbers, rounds them to the storage dtype and lays out
+block tables and pools. It computes none of the method's arithmetic: no
+scores, no softmax, no weighted sums, no rotary embedding. Both the oracle side and
 the GPU side of every test and benchmark read the arrays it returns, so the
 two always see the same stored values.
 
@@ -26,7 +25,6 @@ import numpy as np
 __all__ = [
     "bf16_round",
     "to_storage",
-    "rope_interleaved",
     "draw_block_tables",
     "PrefillCase",
     "DecodeCase",
@@ -36,6 +34,10 @@ __all__ = [
     "paged_decode_case",
     "chunked_paged_prefill_case",
     "mla_case",
+    "AppendCase",
+    "append_case",
+    "MlaAppendCase",
+    "mla_append_case",
     "CONFIG_DESCRIPTIONS",
 ]
 
@@ -65,30 +67,6 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_round(x)
     raise ValueError(f"unknown storage dtype {dtype!r}")
-
-
-def rope_interleaved(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
-    """Interleaved rotary embedding on the last axis of ``x``, in float64.
-
-    The last axis holds pairs ``(x[2i], x[2i+1])``; pair ``i`` at position
-    ``t`` is rotated by the angle ``t * theta**(-2i/d)``, ``d`` being the
-    last-axis width. ``positions`` broadcasts against ``x.shape[:-1]``.
-    This is the pair layout that frink-models 0.31.0 ``src/mla/mod.rs``
-    calls interleaved (module doc, point 2, and ``rotate_pe``).
-    """
-    x = np.asarray(x, dtype=np.float64)
-    d = x.shape[-1]
-    if d % 2:
-        raise ValueError("rotary width must be even")
-    i = np.arange(d // 2, dtype=np.float64)
-    inv_freq = theta ** (-2.0 * i / d)
-    ang = np.asarray(positions, dtype=np.float64)[..., None] * inv_freq
-    c, s = np.cos(ang), np.sin(ang)
-    x0, x1 = x[..., 0::2], x[..., 1::2]
-    out = np.empty_like(x)
-    out[..., 0::2] = x0 * c - x1 * s
-    out[..., 1::2] = x0 * s + x1 * c
-    return out
 
 
 def draw_block_tables(rng: np.random.Generator, seq_lens, block_size: int,
@@ -291,13 +269,16 @@ def chunked_paged_prefill_case(seed: int = 0, *, dtype="bf16", batch=8, cached=3
 
 
 def mla_case(seed: int = 0, *, dtype="bf16", batch=32, ctx=4096, n_heads=128, kv_lora_rank=512,
-             qk_rope_head_dim=64, theta=10000.0, scale=None, seq_lens=None) -> MlaCase:
-    """MLA latent decode: latent rows ``[c | k_rot]`` with ``k_rot`` rotated at its position.
+             qk_rope_head_dim=64, scale=None, seq_lens=None) -> MlaCase:
+    """MLA latent decode: a cache of latent rows ``[c | k_rot]``, every entry iid N(0,1).
 
-    ``c`` and the pre-rotation ``k_rot`` are iid N(0,1); the rotation runs in
-    float64 at each row's own position, then the row is rounded to the
-    storage dtype. ``q_abs`` is iid N(0,1). Default scale is ``1/sqrt(192)``,
-    the un-absorbed query width (128 + 64).
+    The cache stores ``k_rot`` already rotated at each row's position. A
+    rotation of a pair of iid N(0,1) values is again a pair of iid N(0,1)
+    values (the standard normal in the plane is rotation invariant), so the
+    stored rows of a cache filled by rotating iid draws have exactly this
+    distribution; the rotation itself is the append's job. ``q_abs`` is iid
+    N(0,1). Default scale is ``1/sqrt(192)``, the un-absorbed query width
+    (128 + 64).
     """
     rng = np.random.default_rng(seed)
     W = kv_lora_rank + qk_rope_head_dim
@@ -306,13 +287,115 @@ def mla_case(seed: int = 0, *, dtype="bf16", batch=32, ctx=4096, n_heads=128, kv
     else:
         seq_lens = np.asarray(seq_lens, dtype=np.int32)
     q = _normal(rng, (batch, n_heads, W), dtype)
-    lat = rng.standard_normal(size=(batch, ctx, W), dtype=np.float32)
-    pos = np.arange(ctx, dtype=np.float64)[None, :]
-    lat[..., kv_lora_rank:] = rope_interleaved(lat[..., kv_lora_rank:], pos, theta).astype(np.float32)
-    lat = to_storage(lat, dtype)
+    lat = _normal(rng, (batch, ctx, W), dtype)
     if scale is None:
         scale = 1.0 / np.sqrt(192.0)
     return MlaCase(dtype, q, lat, seq_lens, n_heads, kv_lora_rank, qk_rope_head_dim, float(scale))
+
+
+@dataclass
+class AppendCase:
+    """One push into a KV cache: ``n_new`` rows per sequence after ``held[b]`` rows.
+
+    ``k_new``/``v_new`` are ``[B, n_new, Hkv, D]``. Paged: the pools
+    ``[num_blocks, block_size, Hkv, D]`` with tables that already reserve the
+    blocks the new rows need; contiguous: ``[B, capacity, Hkv, D]``. Cache rows
+    not yet written hold NaN.
+    """
+    dtype: str
+    k_new: np.ndarray
+    v_new: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    held: np.ndarray
+    block_table: Optional[np.ndarray]
+    block_size: int
+
+
+def append_case(seed: int = 0, *, dtype="bf16", batch=64, n_new=1, held_lo=511, held_hi=8191,
+                n_kv_heads=8, head_dim=128, block_size=16, paged=True, held=None) -> AppendCase:
+    """A push of ``n_new`` tokens per sequence; ``held`` ~ U[held_lo, held_hi] rows already cached.
+
+    The default is the paged-decode workload's push: 64 sequences that hold
+    511..8191 rows each receive this step's K/V row (so they hold 512..8192
+    after the push). History rows are iid N(0,1) in the storage dtype; rows
+    past the history are NaN.
+    """
+    rng = np.random.default_rng(seed)
+    if held is None:
+        held = rng.integers(held_lo, held_hi + 1, size=batch).astype(np.int32)
+    else:
+        held = np.asarray(held, dtype=np.int32)
+    after = held.astype(np.int64) + n_new
+    row = (n_kv_heads, head_dim)
+    if paged:
+        maxb = int((after.max() + block_size - 1) // block_size)
+        nb, bt = draw_block_tables(rng, after, block_size, 0.10, maxb)
+        kc = np.full((nb, block_size) + row, np.nan, dtype=np.float32)
+        vc = np.full((nb, block_size) + row, np.nan, dtype=np.float32)
+        for b in range(batch):
+            for t0 in range(0, int(held[b]), block_size):
+                n = min(block_size, int(held[b]) - t0)
+                blk = bt[b, t0 // block_size]
+                kc[blk, :n] = _normal(rng, (n,) + row, dtype)
+                vc[blk, :n] = _normal(rng, (n,) + row, dtype)
+    else:
+        bt = None
+        cap = int(after.max())
+        kc = np.full((batch, cap) + row, np.nan, dtype=np.float32)
+        vc = np.full((batch, cap) + row, np.nan, dtype=np.float32)
+        for b in range(batch):
+            kc[b, :held[b]] = _normal(rng, (int(held[b]),) + row, dtype)
+            vc[b, :held[b]] = _normal(rng, (int(held[b]),) + row, dtype)
+    k_new = _normal(rng, (batch, n_new) + row, dtype)
+    v_new = _normal(rng, (batch, n_new) + row, dtype)
+    return AppendCase(dtype, k_new, v_new, kc, vc, held, bt, block_size if paged else 0)
+
+
+@dataclass
+class MlaAppendCase:
+    """One latent push per sequence: ``c_new`` ``[B, R]`` and ``k_rot_new`` ``[B, P]`` (unrotated)
+    into a latent cache (``[B, capacity, R + P]``, or a pool ``[num_blocks, block_size, R + P]``
+    with ``block_table``) that holds ``held[b]`` rows; later rows are NaN."""
+    dtype: str
+    c_new: np.ndarray
+    k_rot_new: np.ndarray
+    latent: np.ndarray
+    held: np.ndarray
+    block_table: Optional[np.ndarray]
+    block_size: int
+    theta: float
+
+
+def mla_append_case(seed: int = 0, *, dtype="bf16", batch=32, held_lo=4095, held_hi=4095,
+                    kv_lora_rank=512, qk_rope_head_dim=64, theta=10000.0, paged=False,
+                    block_size=16, capacity=None, held=None) -> MlaAppendCase:
+    """The MLA decode workload's push: 32 sequences holding 4095 rows get their 4096th."""
+    rng = np.random.default_rng(seed)
+    W = kv_lora_rank + qk_rope_head_dim
+    if held is None:
+        held = rng.integers(held_lo, held_hi + 1, size=batch).astype(np.int32)
+    else:
+        held = np.asarray(held, dtype=np.int32)
+    after = held.astype(np.int64) + 1
+    if paged:
+        maxb = int((after.max() + block_size - 1) // block_size)
+        nb, bt = draw_block_tables(rng, after, block_size, 0.10, maxb)
+        lat = np.full((nb, block_size, W), np.nan, dtype=np.float32)
+        for b in range(batch):
+            for t0 in range(0, int(held[b]), block_size):
+                n = min(block_size, int(held[b]) - t0)
+                lat[bt[b, t0 // block_size], :n] = _normal(rng, (n, W), dtype)
+    else:
+        bt = None
+        cap = int(after.max()) if capacity is None else int(capacity)
+        lat = np.full((batch, cap, W), np.nan, dtype=np.float32)
+        for b in range(batch):
+            lat[b, :held[b]] = _normal(rng, (int(held[b]), W), dtype)
+    c_new = _normal(rng, (batch, kv_lora_rank), dtype)
+    k_rot_new = _normal(rng, (batch, qk_rope_head_dim), dtype)
+    return MlaAppendCase(dtype, c_new, k_rot_new, lat, held, bt, block_size if paged else 0,
+                         float(theta))
 
 
 CONFIG_DESCRIPTIONS = {
@@ -324,5 +407,9 @@ CONFIG_DESCRIPTIONS = {
     "chunked_prefill_paged_bf16": "chunked prefill on paged KV bf16, 8 seqs, 3584 cached + 512 new, "
                                   "H=32 Hkv=8 D=128 block_size 16, scale 0.05, N(0,1)",
     "mla_decode_bf16": "MLA absorbed latent decode bf16, 32 seqs x 4096 ctx, H=128, latent 576 = "
-                       "512 + 64 rotated (theta 1e4), scale 1/sqrt(192), N(0,1)",
+                       "512 + 64 (stored rows iid N(0,1)), scale 1/sqrt(192)",
+    "append_paged_bf16": "push of this step's K/V row into the paged-decode pool: 64 seqs holding "
+                         "511..8191 rows, Hkv=8 D=128 block 16",
+    "mla_append_bf16": "push of the 4096th latent row [c | rope(k_rot)] for 32 seqs, R=512 P=64, "
+                       "theta 1e4",
 }

@@ -1,4 +1,4 @@
-"""The seeded input generators: bf16 rounding, block tables, the latent's RoPE, config shapes."""
+"""The seeded input generators: bf16 rounding, block tables, append cases, config shapes."""
 import numpy as np
 import pytest
 import torch
@@ -48,26 +48,17 @@ def test_paged_decode_full_size_recipe_seed0():
     assert nb == int(np.ceil(1.1 * ((lens + 15) // 16).sum()))
 
 
-def test_rope_interleaved_properties():
-    rng = np.random.default_rng(2)
-    x = rng.standard_normal((5, 64))
-    # position 0 is the identity
-    assert np.array_equal(inputs.rope_interleaved(x, np.zeros(5), 1e4), x)
-    pos = np.arange(5) * 37.0
-    y = inputs.rope_interleaved(x, pos, 1e4)
-    # each pair keeps its length, so the whole row keeps its norm
-    np.testing.assert_allclose(np.hypot(y[:, 0::2], y[:, 1::2]), np.hypot(x[:, 0::2], x[:, 1::2]),
-                               rtol=1e-13)
-    # pair 0 turns by exactly t radians (inverse frequency theta^0 = 1)
-    ang = np.arctan2(y[:, 1], y[:, 0]) - np.arctan2(x[:, 1], x[:, 0])
-    np.testing.assert_allclose(np.cos(ang), np.cos(pos), atol=1e-12)
-    # rotating one shared vector then copying it per head equals rotating each copy
-    heads = np.broadcast_to(x[:, None, :], (5, 3, 64))
-    np.testing.assert_allclose(inputs.rope_interleaved(heads, pos[:, None], 1e4),
-                               np.broadcast_to(y[:, None, :], (5, 3, 64)), rtol=0, atol=0)
-    # a rotation by t1 then t2 is a rotation by t1 + t2
-    z = inputs.rope_interleaved(inputs.rope_interleaved(x, pos, 1e4), pos + 3.0, 1e4)
-    np.testing.assert_allclose(z, inputs.rope_interleaved(x, 2 * pos + 3.0, 1e4), atol=1e-11)
+def test_append_cases_hold_history_and_nan_beyond():
+    c = inputs.append_case(3, batch=4, n_new=3, held_lo=0, held_hi=40, n_kv_heads=2, head_dim=8,
+                           block_size=4)
+    for b in range(4):
+        h = int(c.held[b])
+        for t in range(h + 3):
+            row = c.k_cache[c.block_table[b, t // 4], t % 4]
+            assert np.all(np.isfinite(row)) == (t < h)
+    m = inputs.mla_append_case(3, batch=3, held=[0, 5, 9], kv_lora_rank=16, qk_rope_head_dim=8)
+    assert m.latent.shape == (3, 10, 24) and m.c_new.shape == (3, 16) and m.k_rot_new.shape == (3, 8)
+    assert np.all(np.isnan(m.latent[0])) and np.all(np.isfinite(m.latent[2, :9]))
 
 
 def test_small_case_shapes_and_storage_rounding():

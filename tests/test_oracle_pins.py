@@ -330,3 +330,133 @@ def test_mla_value_is_the_leading_latent_slice():
     lat = rng.standard_normal((1, 6, 12))
     out = O.mla_decode_latent(np.zeros((1, 3, 12)), lat, [6], 9, 0.5)
     np.testing.assert_allclose(out[0], np.broadcast_to(lat[0, :, :9].mean(0), (3, 9)), atol=1e-14)
+
+
+# ---------------------------------------------------------------- cache append and RoPE
+
+ROPE_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rope_append_values.json")
+
+
+def _rope_golden():
+    with open(ROPE_GOLDEN) as f:
+        return json.load(f)
+
+
+def test_golden_rope_unit_vectors():
+    g = _rope_golden()["rope"]
+    for c in g["cases"]:
+        x = np.zeros(g["width"])
+        x[c["unit"]] = 1.0
+        y = O.rope_interleaved(x, c["position"], g["theta"])
+        np.testing.assert_allclose(y[c["expect_at"]], c["expect"], rtol=0, atol=1e-15)
+        # only the unit's own pair moves (interleaved pairs, not split halves)
+        rest = np.delete(y, c["expect_at"])
+        assert np.all(rest == 0.0)
+
+
+def test_rope_identity_at_zero_norm_composition_and_broadcast():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 64))
+    assert np.array_equal(O.rope_interleaved(x, np.zeros(5), 1e4), x)
+    pos = np.arange(5) * 37.0
+    y = O.rope_interleaved(x, pos, 1e4)
+    np.testing.assert_allclose(np.hypot(y[:, 0::2], y[:, 1::2]), np.hypot(x[:, 0::2], x[:, 1::2]),
+                               rtol=1e-13)
+    z = O.rope_interleaved(O.rope_interleaved(x, pos, 1e4), pos + 3.0, 1e4)
+    np.testing.assert_allclose(z, O.rope_interleaved(x, 2 * pos + 3.0, 1e4), atol=1e-11)
+    # rotating the shared vector once, then copying it to every head, equals
+    # rotating every head's copy (the angle depends on the position only)
+    heads = np.broadcast_to(x[:, None, :], (5, 3, 64))
+    np.testing.assert_array_equal(O.rope_interleaved(heads, pos[:, None], 1e4),
+                                  np.broadcast_to(y[:, None, :], (5, 3, 64)))
+
+
+def test_golden_append_paged_and_contiguous():
+    g = _rope_golden()["append_paged"]
+    pool = np.zeros((g["num_blocks"], g["block_size"], 1))
+    rows = np.array(g["new_rows"], dtype=np.float64)[:, :, None]
+    out = O.append_rows(pool, rows, g["positions"], np.array(g["block_table"]), g["block_size"])
+    expect = np.zeros_like(pool)
+    for e in g["expect"]:
+        expect[e["block"], e["row"], 0] = e["value"]
+    assert np.array_equal(out, expect)
+    g = _rope_golden()["append_contiguous"]
+    cache = np.zeros((2, g["capacity"], 1))
+    out = O.append_rows(cache, np.array(g["new_rows"])[:, :, None], g["positions"])
+    expect = np.zeros_like(cache)
+    for e in g["expect"]:
+        expect[e["seq"], e["token"], 0] = e["value"]
+    assert np.array_equal(out, expect)
+
+
+def test_append_then_gather_is_old_rows_then_new_rows():
+    rng = np.random.default_rng(4)
+    B, bs, Hkv, D = 3, 4, 2, 5
+    held = np.array([0, 5, 8])
+    n_new = 3
+    need = (held + n_new + bs - 1) // bs
+    nb = int(need.sum()) + 2
+    perm = rng.permutation(nb)
+    bt = np.full((B, int(need.max())), -1)
+    o = 0
+    for b in range(B):
+        bt[b, :need[b]] = perm[o:o + need[b]]
+        o += need[b]
+    pool = rng.standard_normal((nb, bs, Hkv, D))
+    new = rng.standard_normal((B, n_new, Hkv, D))
+    out = O.append_rows(pool, new, held, bt, bs)
+    written = np.zeros((nb, bs), dtype=bool)
+    for b in range(B):
+        before = O.gather_paged(pool, bt[b], bs, int(held[b]))
+        after = O.gather_paged(out, bt[b], bs, int(held[b]) + n_new)
+        assert np.array_equal(after[:held[b]], before)
+        assert np.array_equal(after[held[b]:], new[b])
+        for t in range(held[b], held[b] + n_new):
+            written[bt[b][t // bs], t % bs] = True
+    # every other pool row is untouched
+    assert np.array_equal(out[~written], pool[~written])
+    # the contiguous form of the same push gathers to the same rows
+    cap = int(held.max()) + n_new
+    cont = np.zeros((B, cap, Hkv, D))
+    for b in range(B):
+        cont[b, :held[b]] = O.gather_paged(pool, bt[b], bs, int(held[b]))
+    cont = O.append_rows(cont, new, held)
+    for b in range(B):
+        L = int(held[b]) + n_new
+        assert np.array_equal(cont[b, :L], O.gather_paged(out, bt[b], bs, L))
+
+
+def test_mla_append_latent_row_layout_and_attention():
+    rng = np.random.default_rng(6)
+    R, P, H, nope, vdim, L = 16, 8, 4, 8, 8, 6
+    theta = 1e4
+    c_hist = rng.standard_normal((L - 1, R))
+    kr_hist = rng.standard_normal((L - 1, P))
+    pos_hist = np.arange(L - 1)
+    latent = np.zeros((1, L + 2, R + P))
+    latent[0, :L - 1] = np.concatenate([c_hist, O.rope_interleaved(kr_hist, pos_hist, theta)], 1)
+    c_new = rng.standard_normal((1, R))
+    kr_new = rng.standard_normal((1, P))
+    out = O.mla_append_latent(latent, c_new, kr_new, [L - 1], theta)
+    assert np.array_equal(out[0, L - 1, :R], c_new[0])
+    np.testing.assert_array_equal(out[0, L - 1, R:], O.rope_interleaved(kr_new[0], L - 1, theta))
+    assert np.array_equal(out[0, :L - 1], latent[0, :L - 1]) and np.all(out[0, L:] == 0)
+    # theta <= 0: the rope-free configuration stores k_rot as given
+    raw = O.mla_append_latent(latent, c_new, kr_new, [L - 1], 0.0)
+    assert np.array_equal(raw[0, L - 1, R:], kr_new[0])
+    # attention over the appended latent (absorbed) equals the naive form in which
+    # every head's key carries its own rotated copy of k_rot
+    q = rng.standard_normal((H, nope + P))
+    w_uk = rng.standard_normal((H, nope, R))
+    w_uv = rng.standard_normal((H, vdim, R))
+    c_all = out[0, :L, :R]
+    kr_all = out[0, :L, R:]
+    scale = 1 / math.sqrt(nope + P)
+    absorbed = O.mla_absorbed(q, c_all, kr_all, w_uk, w_uv, scale)
+    kr_raw = np.concatenate([kr_hist, kr_new], 0)
+    per_head = O.rope_interleaved(np.broadcast_to(kr_raw[:, None, :], (L, H, P)),
+                                  np.arange(L)[:, None], theta)
+    keys = np.concatenate([np.einsum("hnr,lr->lhn", w_uk, c_all), per_head], axis=2)
+    vals = np.einsum("hvr,lr->lhv", w_uv, c_all)
+    naive = O.gqa_attention(q[None], keys, vals, H, H, L - 1, scale)[0]
+    np.testing.assert_allclose(absorbed, naive, rtol=0, atol=1e-12)
