@@ -1,11 +1,13 @@
 /*
  * pkvattn: causal grouped-query attention over a KV cache on MI355X (gfx950).
  *
- * Four operations, one entry point each:
+ * Operations, one entry point each:
  *   attn_prefill        multi-token causal prefill, contiguous or paged K/V
  *   attn_decode_contig  single-token decode over a contiguous cache
  *   attn_decode_paged   single-token decode over a block-table paged cache
  *   mla_decode_latent   absorbed multi-head latent attention decode
+ *   kv_append           push of new K/V rows into a cache or pool
+ *   mla_append_latent   push of an MLA latent row, k_rot rotated once
  *
  * What is computed (kopitiam-runtime 0.2.4, src/attention.rs, module doc
  * "Grouped-query attention" and "Causal masking", fns repeat_kv_heads,
@@ -191,6 +193,61 @@ int attn_decode_paged_noalloc(int dtype, const void* q, const void* k_pool, cons
                               const int32_t* block_table, int max_blocks_per_seq, int block_size,
                               int num_blocks, const int32_t* seq_lens, int max_seq_len,
                               float attention_scale, void* stream);
+
+/*
+ * kv_append: the push of push-then-attend. Writes n_new K and V rows per
+ * sequence into a contiguous cache or a block-table pool, before an
+ * attention call reads them (frink-models 0.38.0 src/decoder/attn_block.rs,
+ * push_and_attend_row: the row is pushed to whichever backing, then
+ * attended; kopitiam-runtime 0.2.4 src/attention.rs, attention_forward
+ * appends to the cache before scoring).
+ *
+ *   k_new, v_new [batch, n_new, n_kv_heads, head_dim]   (dtype)
+ *   positions [batch] int32, device: rows sequence b holds before the push;
+ *            row i becomes token positions[b] + i.
+ *   Contiguous (block_table == NULL): k_cache, v_cache
+ *            [batch, kv_capacity, n_kv_heads, head_dim]; token t of b is row
+ *            (b, t). max_blocks_per_seq, block_size, num_blocks are ignored.
+ *   Paged (block_table != NULL): pools [num_blocks, block_size, n_kv_heads,
+ *            head_dim], block_table [batch, max_blocks_per_seq] int32 device;
+ *            token t of b is row t % block_size of block
+ *            block_table[b][t / block_size] (the caller reserves the blocks
+ *            first). block_size a power of two; kv_capacity is ignored.
+ *   The rows are copied bit for bit; any dtype code and head size. A row
+ *   whose target lies outside the cache (negative position, past kv_capacity
+ *   or the table, or a block id outside [0, num_blocks)) is not written.
+ *   Afterwards the attention calls take seq_lens[b] = positions[b] + n_new.
+ */
+int kv_append(int dtype, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              int batch, int n_kv_heads, int head_dim, int n_new, const int32_t* positions,
+              const int32_t* block_table, int max_blocks_per_seq, int block_size, int num_blocks,
+              int kv_capacity, void* stream);
+
+/*
+ * mla_append_latent: the push of one MLA latent row per sequence
+ * (frink-models 0.31.0 src/mla/mod.rs, mla_forward_token and
+ * absorbed_attention): the row [c | rope(k_rot)] of width
+ * kv_lora_rank + qk_rope_head_dim, where k_rot, shared by every head, is
+ * rotated once at the row's position with the interleaved convention (module
+ * doc point 2, rotate_pe): pair (x[2i], x[2i+1]) turns by
+ * position * rope_theta^(-2i / qk_rope_head_dim). rope_theta <= 0 stores
+ * k_rot as given (the rope-free configuration, module doc point 1).
+ *
+ *   c_new     [batch, kv_lora_rank]        (dtype), copied bit for bit
+ *   k_rot_new [batch, qk_rope_head_dim]    (dtype), not yet rotated; the
+ *             rotation runs in double precision and is rounded once
+ *             (nearest even) to the dtype
+ *   positions [batch] int32, device: the row becomes token positions[b]
+ *   latent: contiguous [batch, kv_capacity, R + P] (block_table == NULL) or a
+ *           pool [num_blocks, block_size, R + P] with block_table as in
+ *           kv_append. Out-of-cache targets are not written.
+ *   qk_rope_head_dim must be even (0 allowed); rope_theta finite.
+ */
+int mla_append_latent(int dtype, const void* c_new, const void* k_rot_new, void* latent,
+                      int batch, int kv_lora_rank, int qk_rope_head_dim,
+                      const int32_t* positions, float rope_theta, const int32_t* block_table,
+                      int max_blocks_per_seq, int block_size, int num_blocks, int kv_capacity,
+                      void* stream);
 
 /*
  * Bytes of device workspace mla_decode_latent needs. Returns 0 for invalid sizes.

@@ -29,6 +29,8 @@ __all__ = [
     "attn_decode_workspace_size",
     "mla_decode_latent",
     "mla_decode_workspace_size",
+    "kv_append",
+    "mla_append_latent",
     "status_string",
     "F32",
     "BF16",
@@ -82,6 +84,12 @@ def lib():
         L.attn_decode_paged_noalloc.restype = i32
         L.attn_decode_paged_noalloc.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, vp, i32, f32, vp]
+        L.kv_append.restype = i32
+        L.kv_append.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32,
+                                i32, vp]
+        L.mla_append_latent.restype = i32
+        L.mla_append_latent.argtypes = [i32, vp, vp, vp, i32, i32, i32, vp, f32, vp, i32, i32, i32,
+                                        i32, vp]
         L.mla_decode_workspace_size.restype = sz
         L.mla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         L.mla_decode_latent.restype = i32
@@ -279,3 +287,61 @@ def mla_decode_latent(q_abs, latent, seq_lens, *, kv_lora_rank: int, max_seq_len
                                  _stream(q_abs, stream))
     _check("mla_decode_latent", st)
     return out
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, positions, *, block_table=None, stream=None):
+    """Write ``k_new``/``v_new`` ``[B, n_new, Hkv, D]`` into the cache at ``positions[b] + i``.
+
+    Contiguous: ``k_cache``/``v_cache`` are ``[B, capacity, Hkv, D]``. Paged: they are pools
+    ``[num_blocks, block_size, Hkv, D]`` and ``block_table`` is int32 ``[B, max_blocks]``.
+    """
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    _i32(positions, "positions")
+    if k_new.shape != v_new.shape or k_cache.shape != v_cache.shape:
+        raise ValueError("k and v must share shapes")
+    if any(t.dtype != k_new.dtype for t in (v_new, k_cache, v_cache)):
+        raise ValueError("k and v must share a dtype")
+    B, n_new, Hkv, D = k_new.shape
+    if tuple(k_cache.shape[2:]) != (Hkv, D):
+        raise ValueError("cache rows must be [n_kv_heads, head_dim]")
+    if block_table is not None:
+        _i32(block_table, "block_table")
+        st = lib().kv_append(_dtype_code(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                             _ptr(v_cache), B, Hkv, D, n_new, _ptr(positions), _ptr(block_table),
+                             block_table.shape[1], k_cache.shape[1], k_cache.shape[0], 0,
+                             _stream(k_new, stream))
+    else:
+        st = lib().kv_append(_dtype_code(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                             _ptr(v_cache), B, Hkv, D, n_new, _ptr(positions), None, 0, 0, 0,
+                             k_cache.shape[1], _stream(k_new, stream))
+    _check("kv_append", st)
+
+
+def mla_append_latent(c_new, k_rot_new, latent, positions, *, rope_theta: float,
+                      block_table=None, stream=None):
+    """Write ``[c_new | rope(k_rot_new)]`` at token ``positions[b]`` of the latent cache.
+
+    ``c_new`` ``[B, R]``, ``k_rot_new`` ``[B, P]`` (unrotated). Contiguous: ``latent`` is
+    ``[B, capacity, R + P]``; paged: a pool ``[num_blocks, block_size, R + P]`` with ``block_table``.
+    """
+    for t, n in ((c_new, "c_new"), (k_rot_new, "k_rot_new"), (latent, "latent")):
+        _dev(t, n)
+    _i32(positions, "positions")
+    if k_rot_new.dtype != c_new.dtype or latent.dtype != c_new.dtype:
+        raise ValueError("c_new, k_rot_new and latent must share a dtype")
+    B, R = c_new.shape
+    P = k_rot_new.shape[1]
+    if latent.shape[-1] != R + P:
+        raise ValueError("latent rows must be kv_lora_rank + qk_rope_head_dim wide")
+    if block_table is not None:
+        _i32(block_table, "block_table")
+        st = lib().mla_append_latent(_dtype_code(c_new), _ptr(c_new), _ptr(k_rot_new), _ptr(latent),
+                                     B, R, P, _ptr(positions), rope_theta, _ptr(block_table),
+                                     block_table.shape[1], latent.shape[1], latent.shape[0], 0,
+                                     _stream(c_new, stream))
+    else:
+        st = lib().mla_append_latent(_dtype_code(c_new), _ptr(c_new), _ptr(k_rot_new), _ptr(latent),
+                                     B, R, P, _ptr(positions), rope_theta, None, 0, 0, 0,
+                                     latent.shape[1], _stream(c_new, stream))
+    _check("mla_append_latent", st)

@@ -267,6 +267,64 @@ int attn_decode_paged_noalloc(int dtype, const void* q, const void* k_pool, cons
                        max_seq_len, attention_scale, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
+int kv_append(int dtype, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              int batch, int n_kv_heads, int head_dim, int n_new, const int32_t* positions,
+              const int32_t* block_table, int max_blocks_per_seq, int block_size, int num_blocks,
+              int kv_capacity, void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!k_new || !v_new || !k_cache || !v_cache || !positions) return PKVA_EINVAL;
+  if (batch < 1 || n_kv_heads < 1 || head_dim < 1 || n_new < 1) return PKVA_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
+  } else {
+    if (kv_capacity < 1) return PKVA_EINVAL;
+  }
+  pkva::AppendParams p{};
+  p.k_new = k_new; p.v_new = v_new; p.k = k_cache; p.v = v_cache;
+  p.positions = positions; p.block_table = block_table;
+  p.batch = batch; p.n_new = n_new;
+  p.row_bytes = (int64_t)n_kv_heads * head_dim * (dtype == PKVA_BF16 ? 2 : 4);
+  p.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  p.block_shift = paged ? log2i(block_size) : 0;
+  p.num_blocks = paged ? num_blocks : 0;
+  p.kv_capacity = paged ? 0 : kv_capacity;
+  const int rc = pkva::launch_kv_append(p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEinval ? PKVA_EINVAL : PKVA_EHIP);
+}
+
+int mla_append_latent(int dtype, const void* c_new, const void* k_rot_new, void* latent, int batch,
+                      int kv_lora_rank, int qk_rope_head_dim, const int32_t* positions,
+                      float rope_theta, const int32_t* block_table, int max_blocks_per_seq,
+                      int block_size, int num_blocks, int kv_capacity, void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!c_new || !latent || !positions) return PKVA_EINVAL;
+  if (qk_rope_head_dim > 0 && !k_rot_new) return PKVA_EINVAL;
+  if (batch < 1 || kv_lora_rank < 1 || qk_rope_head_dim < 0 || qk_rope_head_dim % 2 != 0)
+    return PKVA_EINVAL;
+  if (!std::isfinite(rope_theta)) return PKVA_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
+  } else {
+    if (kv_capacity < 1) return PKVA_EINVAL;
+  }
+  pkva::MlaAppendParams p{};
+  p.rows.k = latent;
+  p.rows.positions = positions; p.rows.block_table = block_table;
+  p.rows.batch = batch; p.rows.n_new = 1;
+  p.rows.row_bytes = (int64_t)(kv_lora_rank + qk_rope_head_dim) * (dtype == PKVA_BF16 ? 2 : 4);
+  p.rows.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  p.rows.block_shift = paged ? log2i(block_size) : 0;
+  p.rows.num_blocks = paged ? num_blocks : 0;
+  p.rows.kv_capacity = paged ? 0 : kv_capacity;
+  p.c_new = c_new; p.k_rot_new = k_rot_new;
+  p.kv_lora_rank = kv_lora_rank; p.rope_dim = qk_rope_head_dim;
+  p.theta = rope_theta;
+  const int rc = pkva::launch_mla_append(p, dtype == PKVA_BF16, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : PKVA_EHIP;
+}
+
 size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
   if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || max_seq_len < 1) return 0;
   if (!pkva::mla_supported(true, kv_lora_rank, 64, n_heads)) return 0;

@@ -81,4 +81,29 @@ int mla_heads_per_group(int n_heads);   // heads served by one workgroup
 int mla_tile_tokens();
 int launch_mla(const MlaParams& p, hipStream_t stream);
 
+// The push into a KV cache (contiguous when block_table is null, else a pool).
+struct AppendParams {
+  const void* k_new;          // [batch, n_new, row] new rows (K)
+  const void* v_new;          // [batch, n_new, row] new rows (V); unused by the latent push
+  void* k;                    // contiguous [batch, cap, row] or pool [nb, bs, row]
+  void* v;
+  const int32_t* positions;   // [batch] rows held before the push
+  const int32_t* block_table; // [batch, max_blocks_per_seq] or null
+  int batch, n_new;
+  int64_t row_bytes;          // bytes of one token row
+  int max_blocks_per_seq, block_shift, num_blocks;
+  int kv_capacity;
+};
+
+struct MlaAppendParams {
+  AppendParams rows;          // k = the latent cache or pool, n_new = 1
+  const void* c_new;          // [batch, kv_lora_rank]
+  const void* k_rot_new;      // [batch, rope_dim], not yet rotated
+  int kv_lora_rank, rope_dim;
+  double theta;               // <= 0: no rotation
+};
+
+int launch_kv_append(const AppendParams& p, hipStream_t stream);
+int launch_mla_append(const MlaAppendParams& p, bool bf16, hipStream_t stream);
+
 }  // namespace pkva

@@ -293,6 +293,18 @@ def mla_case(seed: int = 0, *, dtype="bf16", batch=32, ctx=4096, n_heads=128, kv
     return MlaCase(dtype, q, lat, seq_lens, n_heads, kv_lora_rank, qk_rope_head_dim, float(scale))
 
 
+def _history_rows(bt, held, num_blocks, block_size):
+    """[num_blocks, block_size] mask of the pool rows that hold a sequence's history."""
+    live = np.zeros((num_blocks, block_size), dtype=bool)
+    for b in range(len(held)):
+        h = int(held[b])
+        full, rest = divmod(h, block_size)
+        live[bt[b, :full]] = True
+        if rest:
+            live[bt[b, full], :rest] = True
+    return live
+
+
 @dataclass
 class AppendCase:
     """One push into a KV cache: ``n_new`` rows per sequence after ``held[b]`` rows.
@@ -331,14 +343,11 @@ def append_case(seed: int = 0, *, dtype="bf16", batch=64, n_new=1, held_lo=511, 
     if paged:
         maxb = int((after.max() + block_size - 1) // block_size)
         nb, bt = draw_block_tables(rng, after, block_size, 0.10, maxb)
-        kc = np.full((nb, block_size) + row, np.nan, dtype=np.float32)
-        vc = np.full((nb, block_size) + row, np.nan, dtype=np.float32)
-        for b in range(batch):
-            for t0 in range(0, int(held[b]), block_size):
-                n = min(block_size, int(held[b]) - t0)
-                blk = bt[b, t0 // block_size]
-                kc[blk, :n] = _normal(rng, (n,) + row, dtype)
-                vc[blk, :n] = _normal(rng, (n,) + row, dtype)
+        kc = _normal(rng, (nb, block_size) + row, dtype)
+        vc = _normal(rng, (nb, block_size) + row, dtype)
+        live = _history_rows(bt, held, nb, block_size)
+        kc[~live] = np.nan
+        vc[~live] = np.nan
     else:
         bt = None
         cap = int(after.max())
@@ -381,11 +390,8 @@ def mla_append_case(seed: int = 0, *, dtype="bf16", batch=32, held_lo=4095, held
     if paged:
         maxb = int((after.max() + block_size - 1) // block_size)
         nb, bt = draw_block_tables(rng, after, block_size, 0.10, maxb)
-        lat = np.full((nb, block_size, W), np.nan, dtype=np.float32)
-        for b in range(batch):
-            for t0 in range(0, int(held[b]), block_size):
-                n = min(block_size, int(held[b]) - t0)
-                lat[bt[b, t0 // block_size], :n] = _normal(rng, (n, W), dtype)
+        lat = _normal(rng, (nb, block_size, W), dtype)
+        lat[~_history_rows(bt, held, nb, block_size)] = np.nan
     else:
         bt = None
         cap = int(after.max()) if capacity is None else int(capacity)
