@@ -49,6 +49,7 @@ __all__ = [
     "mla_decode_latent",
     "mla_naive",
     "mla_absorbed",
+    "prefill_varlen",
     "rope_interleaved",
     "append_rows",
     "mla_append_latent",
@@ -159,6 +160,40 @@ def prefill(q, k, v, n_heads, n_kv_heads, seq_kv, position_offset, scale,
             for n, i in enumerate(qsel):
                 out[b, n] = gqa_attention(q[b, i:i + 1], kb, vb, n_heads, n_kv_heads,
                                           position_offset + i, scale)[0]
+    return out
+
+
+def prefill_varlen(q, k, v, cu_q, seq_kv, n_heads, n_kv_heads, scale, block_table=None,
+                   block_size=0, rows=None):
+    """Causal prefill of a ragged batch: ``q`` packs every chunk ``[total_q, H, D]``.
+
+    Sequence ``b`` owns query rows ``cu_q[b] .. cu_q[b+1]-1`` and holds
+    ``seq_kv[b]`` keys (contiguous ``[B, capacity, Hkv, D]`` or gathered
+    through ``block_table``); its chunk is the last ``n_b`` tokens, so its
+    rows sit at offset ``seq_kv[b] - n_b``, and each sequence is the plain
+    causal GQA of :func:`gqa_attention` on its own (the multi-sequence
+    caller of frink-models 0.38.0 ``src/decoder/attn_block.rs``, ``KvStep``).
+    ``rows`` optionally restricts the result to these packed rows.
+    Returns ``[total_q, H, D]`` (or the selected rows).
+    """
+    total = int(cu_q[-1])
+    want = range(total) if rows is None else rows
+    pick = {r: n for n, r in enumerate(want)}
+    out = np.zeros((len(pick),) + q.shape[1:], dtype=np.float64)
+    for b in range(len(seq_kv)):
+        s0, s1, L = int(cu_q[b]), int(cu_q[b + 1]), int(seq_kv[b])
+        mine = [r for r in range(s0, s1) if r in pick]
+        if not mine:
+            continue
+        if block_table is None:
+            kb, vb = k[b, :L], v[b, :L]
+        else:
+            kb = gather_paged(k, block_table[b], block_size, L)
+            vb = gather_paged(v, block_table[b], block_size, L)
+        off = L - (s1 - s0)
+        for r in mine:
+            out[pick[r]] = gqa_attention(q[r:r + 1], kb, vb, n_heads, n_kv_heads, off + r - s0,
+                                         scale)[0]
     return out
 
 

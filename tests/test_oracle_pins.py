@@ -460,3 +460,33 @@ def test_mla_append_latent_row_layout_and_attention():
     vals = np.einsum("hvr,lr->lhv", w_uv, c_all)
     naive = O.gqa_attention(q[None], keys, vals, H, H, L - 1, scale)[0]
     np.testing.assert_allclose(absorbed, naive, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- ragged prefill
+
+def test_prefill_varlen_reduces_to_batched_and_to_brute_force():
+    rng = np.random.default_rng(8)
+    H, Hkv, D = 4, 2, 3
+    # equal chunks and histories: the batched prefill
+    B, n, held = 3, 4, 5
+    q = rng.standard_normal((B, n, H, D))
+    k = rng.standard_normal((B, held + n, Hkv, D))
+    v = rng.standard_normal((B, held + n, Hkv, D))
+    cu = np.arange(B + 1) * n
+    got = O.prefill_varlen(q.reshape(B * n, H, D), k, v, cu, [held + n] * B, H, Hkv, 0.7)
+    ref = O.prefill(q, k, v, H, Hkv, held + n, held, 0.7)
+    np.testing.assert_allclose(got, ref.reshape(B * n, H, D), rtol=0, atol=1e-14)
+    # ragged: every row against the scalar brute force at its own position
+    lens, hist = [0, 3, 1, 5], [4, 0, 7, 2]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    skv = [a + b for a, b in zip(lens, hist)]
+    q = rng.standard_normal((cu[-1], H, D))
+    k = rng.standard_normal((4, max(skv), Hkv, D))
+    v = rng.standard_normal((4, max(skv), Hkv, D))
+    got = O.prefill_varlen(q, k, v, cu, skv, H, Hkv, 0.9)
+    for b in range(4):
+        for i in range(lens[b]):
+            r = cu[b] + i
+            exp = brute.gqa_attention(q[r:r + 1].tolist(), k[b, :skv[b]].tolist(),
+                                  v[b, :skv[b]].tolist(), H, Hkv, hist[b] + i, 0.9)
+            np.testing.assert_allclose(got[r], np.array(exp)[0], rtol=0, atol=1e-12)
