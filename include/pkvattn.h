@@ -3,6 +3,7 @@
  *
  * Operations, one entry point each:
  *   attn_prefill        multi-token causal prefill, contiguous or paged K/V
+ *   attn_prefill_varlen ragged batch of prefill chunks over one shared cache
  *   attn_decode_contig  single-token decode over a contiguous cache
  *   attn_decode_paged   single-token decode over a block-table paged cache
  *   mla_decode_latent   absorbed multi-head latent attention decode
@@ -114,6 +115,41 @@ int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o
                  int seq_q, int seq_kv, int position_offset, float attention_scale,
                  const int32_t* block_table, int max_blocks_per_seq, int block_size,
                  int num_blocks, int kv_capacity, void* stream);
+
+/*
+ * attn_prefill_varlen: causal GQA prefill of a ragged batch, every sequence
+ * with its own chunk length and history, over one shared cache (the batched
+ * and paged multi-sequence caller: frink-models 0.38.0
+ * src/decoder/attn_block.rs, KvStep::Batched and KvStep::Paged, "one
+ * sequence of a multi-sequence batch"; the mask is kopitiam-runtime 0.2.4
+ * src/attention.rs, causal_mask, per sequence).
+ *
+ *   q, o  [total_q, n_heads, head_dim] (dtype): the chunks' query rows packed
+ *         in sequence order.
+ *   cu_seqlens_q [batch + 1] int32, device: sequence b owns rows
+ *         cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (its chunk length n_b may
+ *         be 0); 0 <= cu_seqlens_q[b] <= cu_seqlens_q[b+1] <= total_q.
+ *   seq_kv [batch] int32, device: keys of sequence b, its chunk's rows
+ *         already pushed as the last n_b of them; row i sits at position
+ *         seq_kv[b] - n_b + i and sees keys 0 .. that position.
+ *   max_seq_q: host bound on every n_b (sizes the launch).
+ *   k, v: pools [num_blocks, block_size, n_kv_heads, head_dim] with
+ *         block_table [batch, max_blocks_per_seq] (as attn_prefill), or
+ *         contiguous [batch, kv_capacity, n_kv_heads, head_dim] when
+ *         block_table is NULL.
+ *   Device-side bad data never causes an out-of-bounds access: a sequence
+ *   whose rows leave [0, total_q) is skipped (its rows are not written); one
+ *   with seq_kv[b] < n_b, seq_kv[b] beyond the cache, n_b > max_seq_q or a
+ *   needed block id outside the pool gets NaN rows.
+ *   For equal chunk lengths and histories the result is bitwise that of
+ *   attn_prefill. Built: as attn_prefill.
+ */
+int attn_prefill_varlen(int dtype, const void* q, const void* k, const void* v, void* o,
+                        int batch, int n_heads, int n_kv_heads, int head_dim,
+                        const int32_t* cu_seqlens_q, const int32_t* seq_kv, int total_q,
+                        int max_seq_q, float attention_scale, const int32_t* block_table,
+                        int max_blocks_per_seq, int block_size, int num_blocks, int kv_capacity,
+                        void* stream);
 
 /*
  * Bytes of device workspace attn_decode_contig / attn_decode_paged need for

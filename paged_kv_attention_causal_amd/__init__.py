@@ -23,6 +23,7 @@ __all__ = [
     "lib",
     "header_symbols",
     "attn_prefill",
+    "attn_prefill_varlen",
     "attn_decode_contig",
     "attn_decode_paged",
     "attn_decode_paged_noalloc",
@@ -73,6 +74,9 @@ def lib():
         L.attn_prefill.restype = i32
         L.attn_prefill.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                    vp, i32, i32, i32, i32, vp]
+        L.attn_prefill_varlen.restype = i32
+        L.attn_prefill_varlen.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32,
+                                          f32, vp, i32, i32, i32, i32, vp]
         L.attn_decode_workspace_size.restype = sz
         L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         L.attn_decode_contig.restype = i32
@@ -186,6 +190,43 @@ def attn_prefill(q, k, v, *, seq_kv: int, position_offset: int, attention_scale:
                                 seq_q, seq_kv, position_offset, attention_scale, None, 0, 0, 0,
                                 k.shape[1], _stream(q, stream))
     _check("attn_prefill", st)
+    return out
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens_q, seq_kv, *, max_seq_q: int, attention_scale: float,
+                        block_table=None, out=None, stream=None):
+    """Causal GQA prefill of a ragged batch; returns ``o`` ``[total_q, H, D]``.
+
+    ``q`` packs every sequence's chunk ``[total_q, H, D]``; ``cu_seqlens_q`` (int32
+    ``[B + 1]``) gives each sequence's first row; ``seq_kv`` (int32 ``[B]``) its keys, the
+    chunk being the last of them. Paged: ``k``/``v`` pools ``[num_blocks, block_size, Hkv, D]``
+    with ``block_table``; contiguous: ``[B, capacity, Hkv, D]``.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    _i32(cu_seqlens_q, "cu_seqlens_q")
+    _i32(seq_kv, "seq_kv")
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != v.shape:
+        raise ValueError("q, k, v must share a dtype and k, v a shape")
+    total_q, H, D = q.shape
+    B = seq_kv.shape[0]
+    if cu_seqlens_q.shape[0] != B + 1:
+        raise ValueError("cu_seqlens_q must hold batch + 1 entries")
+    Hkv = k.shape[2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out")
+    if block_table is not None:
+        _i32(block_table, "block_table")
+        st = lib().attn_prefill_varlen(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H,
+                                       Hkv, D, _ptr(cu_seqlens_q), _ptr(seq_kv), total_q, max_seq_q,
+                                       attention_scale, _ptr(block_table), block_table.shape[1],
+                                       k.shape[1], k.shape[0], 0, _stream(q, stream))
+    else:
+        st = lib().attn_prefill_varlen(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H,
+                                       Hkv, D, _ptr(cu_seqlens_q), _ptr(seq_kv), total_q, max_seq_q,
+                                       attention_scale, None, 0, 0, 0, k.shape[1],
+                                       _stream(q, stream))
+    _check("attn_prefill_varlen", st)
     return out
 
 

@@ -174,6 +174,48 @@ int attn_prefill(int dtype, const void* q, const void* k, const void* v, void* o
   return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
 }
 
+int attn_prefill_varlen(int dtype, const void* q, const void* k, const void* v, void* o,
+                        int batch, int n_heads, int n_kv_heads, int head_dim,
+                        const int32_t* cu_seqlens_q, const int32_t* seq_kv, int total_q,
+                        int max_seq_q, float attention_scale, const int32_t* block_table,
+                        int max_blocks_per_seq, int block_size, int num_blocks, int kv_capacity,
+                        void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!q || !k || !v || !o || !cu_seqlens_q || !seq_kv) return PKVA_EINVAL;
+  if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim)) return PKVA_EINVAL;
+  if (total_q < 1 || max_seq_q < 1) return PKVA_EINVAL;
+  if (!scale_ok(attention_scale)) return PKVA_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
+    if ((int64_t)max_blocks_per_seq * block_size > INT_MAX / 2) return PKVA_EINVAL;
+    if ((int64_t)num_blocks * block_size > INT_MAX) return PKVA_EINVAL;   // pool rows index in 31 bits
+  } else {
+    if (kv_capacity < 1 || kv_capacity > INT_MAX / 2) return PKVA_EINVAL;
+    if ((int64_t)batch * kv_capacity > INT_MAX) return PKVA_EINVAL;       // cache rows index in 31 bits
+  }
+  const bool bf16 = dtype == PKVA_BF16;
+  if (!pkva::prefill_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
+  const int64_t q_tiles = ceil_div(max_seq_q, pkva::prefill_block_m());
+  if (q_tiles * batch * n_heads > kMaxGrid) return PKVA_EINVAL;
+
+  pkva::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o;
+  p.block_table = block_table;
+  p.batch = batch; p.n_heads = n_heads; p.n_kv_heads = n_kv_heads;
+  p.group = n_heads / n_kv_heads;
+  p.seq_q = max_seq_q; p.seq_kv = 0; p.position_offset = 0;
+  p.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  p.block_shift = paged ? log2i(block_size) : 0;
+  p.num_blocks = paged ? num_blocks : 0;
+  p.kv_capacity = paged ? 0 : kv_capacity;
+  p.q_tiles = (int)q_tiles;
+  p.scale_log2 = scale_log2(attention_scale);
+  p.cu_q = cu_seqlens_q; p.kv_lens = seq_kv; p.total_q = total_q;
+  const int rc = pkva::launch_prefill(bf16, paged, head_dim, p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
+}
+
 size_t attn_decode_workspace_size(int batch, int n_heads, int n_kv_heads, int head_dim,
                                   int max_seq_len) {
   if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim) || max_seq_len < 1) return 0;

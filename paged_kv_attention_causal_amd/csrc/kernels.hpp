@@ -58,6 +58,10 @@ struct PrefillParams {
   int kv_capacity;
   int q_tiles;                // ceil(seq_q / BLOCK_M)
   float scale_log2;
+  // Ragged batch (null cu_q: every sequence has seq_q, seq_kv, position_offset):
+  const int32_t* cu_q;        // [batch + 1] first query row of each sequence in q and o
+  const int32_t* kv_lens;     // [batch] keys of each sequence (its chunk is the last rows)
+  int total_q;                // rows of q and o; seq_q is then the host bound on a chunk
 };
 
 bool prefill_supported(bool bf16, int head_dim);

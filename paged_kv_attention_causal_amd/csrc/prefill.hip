@@ -80,7 +80,7 @@ __device__ __forceinline__ bf16x4_t ds_read_tr16(const void* p) {
   return __builtin_bit_cast(bf16x4_t, v);
 }
 
-template <bool BF16, int D, bool PAGED>
+template <bool BF16, int D, bool PAGED, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   using M = Mfma<BF16>;
   using T = typename M::Elem;
@@ -128,24 +128,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     }
   }
   const int per_level = p.batch * p.n_heads;
-  const int qt = p.q_tiles - 1 - work / per_level;
+  const int level = work / per_level;
   const int rest = work % per_level;
   const int h = rest % p.n_heads;
   const int b = rest / p.n_heads;
   const int kvh = h / p.group;
 
+  // The sequence's query rows, keys and offset: shared by the batch, or
+  // (ragged batch) its own, with its query rows packed after the previous
+  // sequence's and the chunk being the last seq_q of its seq_kv tokens.
+  int seq_q = p.seq_q, seq_kv = p.seq_kv, off = p.position_offset;
+  int64_t q_row0 = (int64_t)b * p.seq_q;   // the sequence's first row of q and o
+  int qt;                                    // query tile of this work item
+  bool poisoned = false;                     // bad sizes or block ids: NaN rows
+  if constexpr (VARLEN) {
+    const int s0 = p.cu_q[b], s1 = p.cu_q[b + 1];
+    // Rows outside [0, total_q): nothing of this sequence can be written.
+    if (s0 < 0 || s1 < s0 || s1 > p.total_q) return;
+    seq_q = s1 - s0;
+    q_row0 = s0;
+    seq_kv = p.kv_lens[b];
+    off = seq_kv - seq_q;
+    // Tile levels count from each sequence's last (heaviest) tile.
+    qt = (seq_q + kBlockM - 1) / kBlockM - 1 - level;
+    if (qt < 0) return;   // uniform over the workgroup
+    const int64_t cap = PAGED ? (int64_t)p.max_blocks_per_seq << p.block_shift : p.kv_capacity;
+    poisoned = off < 0 || seq_kv > cap || seq_q > p.seq_q;
+  } else {
+    qt = p.q_tiles - 1 - level;
+  }
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
   const int q0 = qt * kBlockM;
-  const int off = p.position_offset;
   const uint32_t row_bytes = (uint32_t)(p.n_kv_heads * ROWB);
   const int shift = p.block_shift;
   const int bs_mask = (1 << shift) - 1;
 
   // Keys this tile can see: 0 .. last_key.
-  const int q_last = min(q0 + kBlockM, p.seq_q) - 1;
-  const int last_key = min(p.seq_kv - 1, off + q_last);
+  const int q_last = min(q0 + kBlockM, seq_q) - 1;
+  const int last_key = min(seq_kv - 1, off + q_last);
   const int n_kt = last_key / kBlockN + 1;
 
   const char* kg = (const char*)p.k + (int64_t)kvh * ROWB;
@@ -208,10 +231,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  bool poisoned = false;
   if constexpr (PAGED) {
-    load_window(0);
-    poisoned = s_bad != 0;
+    if (!poisoned) {
+      load_window(0);
+      poisoned = s_bad != 0;
+    }
   }
 
   if (!poisoned) {
@@ -219,13 +243,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const int qrow = q0 + wave * 32 + lr;
     typename M::Op qB[KSTEPS];
     {
-      const T* qgp = (const T*)p.q + (((int64_t)b * p.seq_q + qrow) * p.n_heads + h) * D;
+      const T* qgp = (const T*)p.q + ((q_row0 + qrow) * p.n_heads + h) * D;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         if constexpr (BF16) {
-          qB[kk] = qrow < p.seq_q ? *(const bf16x8_t*)(qgp + kk * 16 + hf * 8) : bf16x8_t{};
+          qB[kk] = qrow < seq_q ? *(const bf16x8_t*)(qgp + kk * 16 + hf * 8) : bf16x8_t{};
         } else {
-          qB[kk] = qrow < p.seq_q ? qgp[kk * 2 + hf] : 0.0f;
+          qB[kk] = qrow < seq_q ? qgp[kk * 2 + hf] : 0.0f;
         }
       }
     }
@@ -238,11 +262,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const float c = p.scale_log2;
     const int wave_pos_first = off + q0 + wave * 32;
     const int my_pos = off + qrow;
-    const bool wave_live = q0 + wave * 32 < p.seq_q;
+    const bool wave_live = q0 + wave * 32 < seq_q;
     // Tiles this wave computes (0 .. n_w - 1), and the first one that needs
     // the mask (crosses the wave's diagonal or the end of the keys).
     const int n_w = wave_live ? min(n_kt, (wave_pos_first + 31) / kBlockN + 1) : 0;
-    const int kt_open = min(min((wave_pos_first + 1) / kBlockN, p.seq_kv / kBlockN), n_w);
+    const int kt_open = min(min((wave_pos_first + 1) / kBlockN, seq_kv / kBlockN), n_w);
 
     // S^T = K Q^T for the K tile at sK.
     auto qk = [&](const char* sK, f32x16_t (&s)[2]) {
@@ -265,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     };
     // Accumulator register r of key block kb holds key k0 + 32*kb + 8*(r/4) + 4*hf + r%4.
     auto mask = [&](int k0, f32x16_t (&s)[2]) {
-      const int lim = min(my_pos, p.seq_kv - 1) - (k0 + 4 * hf);
+      const int lim = min(my_pos, seq_kv - 1) - (k0 + 4 * hf);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -460,13 +484,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // A wave reads back only its own rows, after its own LDS writes (LDS
       // operations of one wave complete in order).
       const int row0 = q0 + wave * 32;       // the wave's first query row (uniform)
-      char* og = (char*)p.o + ((((int64_t)b * p.seq_q + row0) * p.n_heads + h) * D) * ESZ;
+      char* og = (char*)p.o + (((q_row0 + row0) * p.n_heads + h) * D) * ESZ;
       const uint32_t ostride = (uint32_t)(p.n_heads * ROWB);   // bytes between query rows
       const int rr0 = lane / CPR, cc = lane % CPR;
 #pragma unroll
       for (int r0 = 0; r0 < 32; r0 += ORP) {
         const int rr = r0 + rr0;
-        if (row0 + rr < p.seq_q) {
+        if (row0 + rr < seq_q) {
           const u32x4_t v = *(const u32x4_t*)(s_out + rr * OROW + cc * 16);
           store_nt((u32x4_t*)(og + (uint32_t)rr * ostride + cc * 16), v);
         }
@@ -478,8 +502,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   // A needed block lies outside the pool: NaN rows for this (sequence, head).
   for (int idx = tid; idx < kBlockM * D; idx += kThreads) {
     const int i = q0 + idx / D;
-    if (i < p.seq_q) {
-      const int64_t o = (((int64_t)b * p.seq_q + i) * p.n_heads + h) * D + idx % D;
+    if (i < seq_q) {
+      const int64_t o = ((q_row0 + i) * p.n_heads + h) * D + idx % D;
       ((T*)p.o)[o] = (T)__builtin_nanf("");
     }
   }
@@ -488,7 +512,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 template <bool BF16, int D, bool PAGED>
 int launch_t(const PrefillParams& p, hipStream_t stream) {
   const int grid = p.q_tiles * p.batch * p.n_heads;
-  hipLaunchKernelGGL((prefill_kernel<BF16, D, PAGED>), dim3(grid), dim3(kThreads), 0, stream, p);
+  if (p.cu_q != nullptr) {
+    hipLaunchKernelGGL((prefill_kernel<BF16, D, PAGED, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<BF16, D, PAGED, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, p);
+  }
   return hipGetLastError() == hipSuccess ? kOk : kEhip;
 }
 

@@ -34,6 +34,8 @@ __all__ = [
     "paged_decode_case",
     "chunked_paged_prefill_case",
     "mla_case",
+    "VarlenPrefillCase",
+    "varlen_prefill_case",
     "AppendCase",
     "append_case",
     "MlaAppendCase",
@@ -306,6 +308,73 @@ def _history_rows(bt, held, num_blocks, block_size):
 
 
 @dataclass
+class VarlenPrefillCase:
+    """A ragged batch of prefill chunks over one shared cache.
+
+    Sequence ``b`` holds ``seq_kv[b]`` tokens; its chunk is the last
+    ``q_lens[b]`` of them (already pushed), at positions
+    ``seq_kv[b] - q_lens[b] ..``. ``q`` packs the chunks' query rows
+    ``[sum(q_lens), H, D]`` in sequence order; ``cu_q`` is
+    ``[0, q_lens[0], q_lens[0] + q_lens[1], ...]``. Paged: ``k``/``v`` are pools
+    ``[num_blocks, block_size, Hkv, D]``; contiguous (``block_table`` None):
+    ``[B, capacity, Hkv, D]``.
+    """
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cu_q: np.ndarray
+    seq_kv: np.ndarray
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    scale: float
+    block_table: Optional[np.ndarray] = None
+    block_size: int = 0
+
+    @property
+    def batch(self) -> int:
+        return len(self.seq_kv)
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.cu_q)
+
+
+def varlen_prefill_case(seed: int = 0, *, dtype="bf16", q_lens=None, cached=None, batch=16,
+                        q_lo=1, q_hi=1024, cached_lo=0, cached_hi=4096, n_heads=32, n_kv_heads=8,
+                        head_dim=128, block_size=16, paged=True, scale=None, slack=0.10,
+                        std=1.0) -> VarlenPrefillCase:
+    """Ragged chunks: ``q_lens`` ~ U[q_lo, q_hi] new tokens after ``cached`` ~ U[cached_lo,
+    cached_hi] cached ones per sequence (both ends included), unless given."""
+    rng = np.random.default_rng(seed)
+    if q_lens is None:
+        q_lens = rng.integers(q_lo, q_hi + 1, size=batch)
+    if cached is None:
+        cached = rng.integers(cached_lo, cached_hi + 1, size=len(q_lens))
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    cached = np.asarray(cached, dtype=np.int64)
+    seq_kv = (q_lens + cached).astype(np.int32)
+    B = len(q_lens)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    row = (n_kv_heads, head_dim)
+    if paged:
+        nb, bt = draw_block_tables(rng, seq_kv, block_size, slack)
+        k = _normal(rng, (nb, block_size) + row, dtype, std)
+        v = _normal(rng, (nb, block_size) + row, dtype, std)
+    else:
+        bt = None
+        cap = int(seq_kv.max())
+        k = _normal(rng, (B, cap) + row, dtype, std)
+        v = _normal(rng, (B, cap) + row, dtype, std)
+    q = _normal(rng, (int(cu_q[-1]), n_heads, head_dim), dtype, std)
+    if scale is None:
+        scale = 1.0 / np.sqrt(head_dim)
+    return VarlenPrefillCase(dtype, q, k, v, cu_q, seq_kv, n_heads, n_kv_heads, head_dim,
+                             float(scale), bt, block_size if paged else 0)
+
+
+@dataclass
 class AppendCase:
     """One push into a KV cache: ``n_new`` rows per sequence after ``held[b]`` rows.
 
@@ -414,6 +483,9 @@ CONFIG_DESCRIPTIONS = {
                                   "H=32 Hkv=8 D=128 block_size 16, scale 0.05, N(0,1)",
     "mla_decode_bf16": "MLA absorbed latent decode bf16, 32 seqs x 4096 ctx, H=128, latent 576 = "
                        "512 + 64 (stored rows iid N(0,1)), scale 1/sqrt(192)",
+    "varlen_prefill_paged_bf16": "ragged chunked prefill bf16 over one paged pool: 16 seqs, chunk "
+                                 "U[1,1024] after U[0,4096] cached, H=32 Hkv=8 D=128 block 16, "
+                                 "scale 1/sqrt(128), N(0,1)",
     "append_paged_bf16": "push of this step's K/V row into the paged-decode pool: 64 seqs holding "
                          "511..8191 rows, Hkv=8 D=128 block 16",
     "mla_append_bf16": "push of the 4096th latent row [c | rope(k_rot)] for 32 seqs, R=512 P=64, "

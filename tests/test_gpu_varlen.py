@@ -1,0 +1,122 @@
+"""GPU parity of attn_prefill_varlen (ragged chunks over one shared cache) against the oracle.
+
+Every case compares element by element with the float64 oracle's ragged prefill; a
+ragged batch with equal chunks must match attn_prefill bitwise; bad sequences get NaN
+rows without disturbing the others.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_causal_amd as pk
+from oracle import oracle as O
+from paged_kv_attention_causal_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 2e-3, "bf16": 2e-2}
+
+
+def dev(a, dtype="bf16"):
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(DEV)
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check(got, ref, dtype, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    say(f"  {what}: max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
+    assert err.max() <= TOL[dtype], f"{what}: {err.max():.3e}"
+
+
+def run(c, max_seq_q=None, cu=None, skv=None):
+    bt = i32(c.block_table) if c.block_table is not None else None
+    mq = int(c.q_lens.max()) if max_seq_q is None else max_seq_q
+    return pk.attn_prefill_varlen(dev(c.q, c.dtype), dev(c.k, c.dtype), dev(c.v, c.dtype),
+                                  i32(c.cu_q if cu is None else cu),
+                                  i32(c.seq_kv if skv is None else skv), max_seq_q=max(1, mq),
+                                  attention_scale=c.scale, block_table=bt)
+
+
+CASES = [
+    # (q_lens, cached, H, Hkv, D, bs, dtype)
+    ([1, 300, 0, 77, 513], [0, 1000, 5, 64, 2000], 8, 2, 128, 16, "bf16"),
+    ([256, 257, 255, 1], [0, 3, 700, 4095], 28, 4, 128, 1, "bf16"),
+    ([64, 200, 9], [100, 0, 333], 4, 4, 128, 0, "bf16"),          # contiguous cache
+    ([70, 1, 130], [5, 77, 0], 6, 3, 16, 4, "f32"),
+    ([33, 0, 65], [0, 9, 64], 4, 2, 16, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "q{}_c{}_H{}Hkv{}D{}bs{}{}".format(
+    "-".join(map(str, c[0])), "-".join(map(str, c[1])), *c[2:]))
+def test_varlen_prefill_small(case):
+    q_lens, cached, H, Hkv, D, bs, dtype = case
+    say(f"case: ragged prefill {case}")
+    c = inputs.varlen_prefill_case(31, dtype=dtype, q_lens=q_lens, cached=cached, n_heads=H,
+                                   n_kv_heads=Hkv, head_dim=D, block_size=bs or 16,
+                                   paged=bool(bs), scale=0.3 if dtype == "f32" else None)
+    o = run(c)
+    ref = O.prefill_varlen(c.q, c.k, c.v, c.cu_q, c.seq_kv, H, Hkv, c.scale, c.block_table,
+                           c.block_size)
+    check(host(o), ref, dtype, "ragged prefill")
+
+
+def test_varlen_full_size_mix_sampled_rows():
+    say("case: ragged prefill bf16, 16 seqs, chunks U[1,1024] after U[0,4096] cached, H=32 Hkv=8")
+    c = inputs.varlen_prefill_case(0)
+    o = run(c)
+    o2 = run(c)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), "ragged prefill is not deterministic"
+    rng = np.random.default_rng(3)
+    rows = []
+    for b in range(c.batch):
+        s0, s1 = int(c.cu_q[b]), int(c.cu_q[b + 1])
+        rows += sorted({s0, s1 - 1, *rng.integers(s0, s1, 2).tolist()})
+    ref = O.prefill_varlen(c.q, c.k, c.v, c.cu_q, c.seq_kv, 32, 8, c.scale, c.block_table, 16,
+                           rows=rows)
+    check(host(o)[rows], ref, "bf16", f"{len(rows)} rows over all 16 sequences")
+
+
+def test_varlen_with_equal_chunks_is_bitwise_the_batched_prefill():
+    say("case: ragged prefill with equal chunks == attn_prefill (bitwise)")
+    c = inputs.chunked_paged_prefill_case(0, batch=3, cached=700, seq_q=300)
+    B, n = 3, 300
+    q = dev(c.q)
+    k, v, bt = dev(c.k), dev(c.v), i32(c.block_table)
+    ob = pk.attn_prefill(q, k, v, seq_kv=c.seq_kv, position_offset=700, attention_scale=c.scale,
+                         block_table=bt)
+    ov = pk.attn_prefill_varlen(q.reshape(B * n, 32, 128), k, v, i32(np.arange(B + 1) * n),
+                                i32([c.seq_kv] * B), max_seq_q=n, attention_scale=c.scale,
+                                block_table=bt)
+    assert torch.equal(ov.reshape(B, n, 32, 128), ob)
+
+
+def test_varlen_bad_sequences_get_nan_rows_only():
+    say("case: ragged prefill with a too-short history and an out-of-pool block")
+    c = inputs.varlen_prefill_case(5, q_lens=[40, 50, 60], cached=[10, 20, 30], n_heads=4,
+                                   n_kv_heads=2, block_size=16)
+    skv = c.seq_kv.copy()
+    skv[0] = 39                      # fewer keys than chunk rows
+    bt = c.block_table.copy()
+    bt[2, 1] = c.k.shape[0] + 1      # a needed block outside the pool
+    o = host(pk.attn_prefill_varlen(dev(c.q), dev(c.k), dev(c.v), i32(c.cu_q), i32(skv),
+                                    max_seq_q=60, attention_scale=c.scale, block_table=i32(bt)))
+    assert np.all(np.isnan(o[0:40])) and np.all(np.isnan(o[90:150]))
+    ref = O.prefill_varlen(c.q, c.k, c.v, c.cu_q, c.seq_kv, 4, 2, c.scale, c.block_table, 16,
+                           rows=list(range(40, 90)))
+    check(o[40:90], ref, "bf16", "the clean sequence")
