@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import math
 
-__all__ = ["gqa_attention"]
+__all__ = ["gqa_attention", "gqa_attention_arms"]
 
 
 def gqa_attention(q, k, v, n_heads, n_kv_heads, position_offset, scale):
@@ -35,6 +35,42 @@ def gqa_attention(q, k, v, n_heads, n_kv_heads, position_offset, scale):
             m = max(s)
             w = [math.exp(x - m) for x in s]
             z = math.fsum(w)
+            row.append([math.fsum(w[n] * float(v[j][g][c]) for n, j in enumerate(visible)) / z
+                        for c in range(dv)])
+        out.append(row)
+    return out
+
+
+def gqa_attention_arms(q, k, v, n_heads, n_kv_heads, position_offset, scale, window=0,
+                       softcap=0.0, alibi=None, sinks=None):
+    """The same with a layer's optional arms: key ``j`` is visible to the row at
+    position ``p`` iff ``j <= p`` and (``window <= 0`` or ``p - j < window``); the
+    logit is ``scale * q.k``, then ``softcap * tanh(logit / softcap)`` if
+    ``softcap > 0``, plus ``alibi[h] * (j - p)``; the softmax denominator also
+    counts ``exp(sinks[h])``, a logit with no value."""
+    assert n_kv_heads > 0 and n_heads % n_kv_heads == 0
+    group = n_heads // n_kv_heads
+    dv = len(v[0][0]) if len(k) else 0
+    out = []
+    for i in range(len(q)):
+        p = position_offset + i
+        visible = [j for j in range(len(k)) if j <= p and (window <= 0 or p - j < window)]
+        row = []
+        for h in range(n_heads):
+            g = h // group
+            logits = []
+            for j in visible:
+                x = scale * math.fsum(float(q[i][h][c]) * float(k[j][g][c])
+                                      for c in range(len(q[i][h])))
+                if softcap > 0:
+                    x = softcap * math.tanh(x / softcap)
+                if alibi is not None:
+                    x += float(alibi[h]) * (j - p)
+                logits.append(x)
+            extra = [float(sinks[h])] if sinks is not None else []
+            m = max(logits + extra)
+            w = [math.exp(x - m) for x in logits]
+            z = math.fsum(w + [math.exp(x - m) for x in extra])
             row.append([math.fsum(w[n] * float(v[j][g][c]) for n, j in enumerate(visible)) / z
                         for c in range(dv)])
         out.append(row)

@@ -50,6 +50,8 @@ __all__ = [
     "mla_naive",
     "mla_absorbed",
     "prefill_varlen",
+    "gqa_attention_arms",
+    "decode_arms",
     "rope_interleaved",
     "append_rows",
     "mla_append_latent",
@@ -122,6 +124,85 @@ def gqa_attention(q, k, v, n_heads: int, n_kv_heads: int, position_offset: int,
     probs = masked_softmax(scores, causal_mask(seq_q, seq_kv, position_offset))
     out = np.matmul(probs, v_rep)               # [H, seq_q, Dv]
     return out.transpose(1, 0, 2)
+
+
+def gqa_attention_arms(q, k, v, n_heads: int, n_kv_heads: int, position_offset: int,
+                       scale: float, window: int = 0, softcap: float = 0.0, alibi=None,
+                       sinks=None) -> np.ndarray:
+    """Causal GQA with the optional arms of one attention layer, in float64.
+
+    The arms frink-models 0.38.0 ``src/decoder/attn_block.rs``
+    (``push_and_attend_row``) hands its one kernel besides the plain case,
+    read as their usual definitions (the page names them, it does not spell
+    them out):
+    * ``window > 0``: row ``i`` (position ``p = position_offset + i``) sees
+      only keys ``j`` with ``p - window < j <= p``;
+    * ``softcap > 0``: every logit ``x = scale * q.k`` becomes
+      ``softcap * tanh(x / softcap)``;
+    * ``alibi`` (``[H]`` slopes): head ``h`` adds ``alibi[h] * (j - p)`` to
+      its logits after the softcap;
+    * ``sinks`` (``[H]`` logits): head ``h``'s softmax runs over its visible
+      keys plus one extra logit ``sinks[h]`` that carries no value, so the
+      weights of the keys sum to less than one.
+    ``k`` is ``[seq_kv, Hkv, D]``, ``v`` is ``[seq_kv, Hkv, Dv]`` (``Dv`` may
+    differ from ``D``: the page's ``head_dim`` and ``v_head_dim``). Returns
+    ``[seq_q, H, Dv]``. The steps: head-major, repeat the KV heads, scores,
+    softcap, ALiBi bias, additive mask (causal and window), softmax with the
+    sink, ``P V``.
+    """
+    if n_kv_heads <= 0 or n_heads <= 0 or n_heads % n_kv_heads != 0:
+        raise ValueError("n_heads must be a positive multiple of n_kv_heads")
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    seq_q, seq_kv = q.shape[0], k.shape[0]
+    group_size = n_heads // n_kv_heads
+    qh = q.transpose(1, 0, 2)
+    k_rep = repeat_kv_heads(k.transpose(1, 0, 2), group_size)
+    v_rep = repeat_kv_heads(v.transpose(1, 0, 2), group_size)
+    x = np.matmul(qh, k_rep.transpose(0, 2, 1)) * scale          # [H, seq_q, seq_kv]
+    if softcap > 0:
+        x = softcap * np.tanh(x / softcap)
+    pos = position_offset + np.arange(seq_q)[:, None]            # [seq_q, 1]
+    rel = np.arange(seq_kv)[None, :] - pos                       # j - p
+    if alibi is not None:
+        x = x + np.asarray(alibi, dtype=np.float64)[:, None, None] * rel[None]
+    mask = causal_mask(seq_q, seq_kv, position_offset)
+    if window > 0:
+        mask = np.where(rel[None] <= -window, -np.inf, mask)
+    s = x + mask
+    mx = np.max(s, axis=-1, keepdims=True)
+    if sinks is not None:
+        snk = np.asarray(sinks, dtype=np.float64)[:, None, None]
+        mx = np.maximum(mx, snk)
+    e = np.exp(s - mx)
+    den = np.sum(e, axis=-1, keepdims=True)
+    if sinks is not None:
+        den = den + np.exp(snk - mx)
+    out = np.matmul(e / den, v_rep)
+    return out.transpose(1, 0, 2)
+
+
+def decode_arms(q, k, v, seq_lens, n_heads, n_kv_heads, scale, block_table=None, block_size=0,
+                window=0, softcap=0.0, alibi=None, sinks=None, batch_indices=None):
+    """Single-token decode with the arms of :func:`gqa_attention_arms`.
+
+    Contiguous: ``k``/``v`` are ``[B, capacity, Hkv, D or Dv]``; paged: pools
+    gathered through ``block_table``. The query of sequence ``b`` sits at
+    position ``seq_lens[b] - 1`` (push-then-attend).
+    """
+    idx = range(q.shape[0]) if batch_indices is None else batch_indices
+    out = []
+    for b in idx:
+        L = int(seq_lens[b])
+        if block_table is None:
+            kb, vb = k[b, :L], v[b, :L]
+        else:
+            kb = gather_paged(k, block_table[b], block_size, L)
+            vb = gather_paged(v, block_table[b], block_size, L)
+        out.append(gqa_attention_arms(q[b][None], kb, vb, n_heads, n_kv_heads, L - 1, scale,
+                                      window, softcap, alibi, sinks)[0])
+    return np.stack(out)
 
 
 def gather_paged(pool: np.ndarray, block_table_row: np.ndarray, block_size: int,

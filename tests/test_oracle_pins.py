@@ -490,3 +490,79 @@ def test_prefill_varlen_reduces_to_batched_and_to_brute_force():
             exp = brute.gqa_attention(q[r:r + 1].tolist(), k[b, :skv[b]].tolist(),
                                   v[b, :skv[b]].tolist(), H, Hkv, hist[b] + i, 0.9)
             np.testing.assert_allclose(got[r], np.array(exp)[0], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- attention arms
+
+def test_arms_off_is_the_plain_definition():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((5, 4, 8))
+    k = rng.standard_normal((9, 2, 8))
+    v = rng.standard_normal((9, 2, 6))          # V narrower than K
+    a = O.gqa_attention_arms(q, k, v, 4, 2, 4, 0.4)
+    b = O.gqa_attention(q, k, v, 4, 2, 4, 0.4)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    # a window wider than every distance, zero slopes, a sink at -inf: still plain
+    c = O.gqa_attention_arms(q, k, v, 4, 2, 4, 0.4, window=100, alibi=np.zeros(4),
+                             sinks=np.full(4, -np.inf))
+    np.testing.assert_allclose(c, b, rtol=0, atol=1e-14)
+
+
+def test_arms_window_is_attention_over_the_last_keys():
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 2, 4))
+    k = rng.standard_normal((10, 1, 4))
+    v = rng.standard_normal((10, 1, 4))
+    for w in (1, 3, 7):
+        got = O.gqa_attention_arms(q, k, v, 2, 1, 9, 0.5, window=w)
+        # the plain attention over keys 10-w .. 9, the query being the last of them
+        ref = O.gqa_attention(q, k[10 - w:], v[10 - w:], 2, 1, w - 1, 0.5)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+    # window 1: the query sees its own key only
+    np.testing.assert_array_equal(O.gqa_attention_arms(q, k, v, 2, 1, 9, 0.5, window=1)[0],
+                                  np.repeat(v[9], 2, axis=0))
+
+
+def test_arms_closed_forms_alibi_sinks_softcap():
+    n = 6
+    v = np.eye(n)[:, None, :]                   # one-hot values: the output is the weights
+    k = np.zeros((n, 1, 3))
+    q = np.zeros((1, 1, 3))
+    # zero scores + ALiBi slope m: weights proportional to exp(-m (p - j)), geometric
+    m = 0.7
+    got = O.gqa_attention_arms(q, k, v, 1, 1, n - 1, 1.0, alibi=[m])[0, 0]
+    r = [math.exp(-m * (n - 1 - j)) for j in range(n)]
+    np.testing.assert_allclose(got, np.array(r) / sum(r), rtol=1e-14)
+    # zero scores + a sink s: every key weighs 1 / (n + e^s)
+    s = 1.3
+    got = O.gqa_attention_arms(q, k, v, 1, 1, n - 1, 1.0, sinks=[s])[0, 0]
+    np.testing.assert_allclose(got, np.full(n, 1 / (n + math.exp(s))), rtol=1e-14)
+    # two keys with q.k = 0 and 2, scale 1, softcap 1: logits tanh(0) = 0 and tanh(2)
+    q2 = np.array([[[1.0, 0.0]]])
+    k2 = np.array([[[0.0, 0.0]], [[2.0, 0.0]]])
+    v2 = np.eye(2)[:, None, :]
+    got = O.gqa_attention_arms(q2, k2, v2, 1, 1, 1, 1.0, softcap=1.0)[0, 0]
+    e = math.exp(math.tanh(2.0))
+    np.testing.assert_allclose(got, [1 / (1 + e), e / (1 + e)], rtol=1e-14)
+    # a huge cap is the plain softmax
+    big = O.gqa_attention_arms(q2, k2, v2, 1, 1, 1, 1.0, softcap=1e7)[0, 0]
+    np.testing.assert_allclose(big, [1 / (1 + math.e ** 2), math.e ** 2 / (1 + math.e ** 2)],
+                               rtol=1e-9)
+
+
+def test_arms_match_the_scalar_brute_force():
+    rng = np.random.default_rng(13)
+    for trial in range(8):
+        H, Hkv = [(2, 1), (4, 2), (3, 3), (6, 2)][trial % 4]
+        D, Dv = 1 + trial % 4, 1 + (trial * 3) % 5
+        sq, off = 1 + trial % 3, trial % 5
+        skv = off + sq + (trial % 2)
+        q = rng.standard_normal((sq, H, D))
+        k = rng.standard_normal((skv, Hkv, D))
+        v = rng.standard_normal((skv, Hkv, Dv))
+        kw = dict(window=[0, 2, 3, 1][trial % 4], softcap=[0.0, 0.8, 3.0, 0.0][(trial + 1) % 4],
+                  alibi=rng.uniform(0, 1, H) if trial % 2 else None,
+                  sinks=rng.standard_normal(H) if trial % 3 else None)
+        got = O.gqa_attention_arms(q, k, v, H, Hkv, off, 0.6, **kw)
+        ref = brute.gqa_attention_arms(q.tolist(), k.tolist(), v.tolist(), H, Hkv, off, 0.6, **kw)
+        np.testing.assert_allclose(got, np.array(ref), rtol=0, atol=1e-12)
