@@ -6,6 +6,8 @@
  *   attn_prefill_varlen ragged batch of prefill chunks over one shared cache
  *   attn_decode_contig  single-token decode over a contiguous cache
  *   attn_decode_paged   single-token decode over a block-table paged cache
+ *   attn_decode_*_ext   the same with a layer's arms (window, softcap, ALiBi,
+ *                       sinks, V width)
  *   mla_decode_latent   absorbed multi-head latent attention decode
  *   kv_append           push of new K/V rows into a cache or pool
  *   mla_append_latent   push of an MLA latent row, k_rot rotated once
@@ -206,6 +208,56 @@ int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* 
                       int num_blocks, const int32_t* seq_lens, int max_seq_len,
                       float attention_scale, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * The optional arms of one attention layer (frink-models 0.38.0
+ * src/decoder/attn_block.rs, push_and_attend_row: one kernel serves plain,
+ * windowed, softcapped and sink-bearing layers, with ALiBi slopes, at the
+ * cache's own key and value widths). The page names them; the readings are
+ * their usual definitions. For the query at position p and key j <= p:
+ *   window > 0      only keys with p - window < j <= p are visible; 0: all
+ *   softcap > 0     logit x = attention_scale * q.k becomes
+ *                   softcap * tanh(x / softcap); 0: off
+ *   alibi_slopes    device float [n_heads] or NULL: head h adds
+ *                   alibi_slopes[h] * (j - p) to its logits (after softcap)
+ *   sinks           device float [n_heads] or NULL: head h's softmax also
+ *                   counts exp(sinks[h]), a logit with no value, so its key
+ *                   weights sum to less than one
+ *   v_head_dim      width of the V rows and of o; 0 means head_dim (the K
+ *                   and q width)
+ */
+typedef struct pkva_arms {
+  int window;
+  float softcap;
+  const float* alibi_slopes;
+  const float* sinks;
+  int v_head_dim;
+} pkva_arms;
+
+/*
+ * attn_decode_contig_ext / attn_decode_paged_ext: attn_decode_contig /
+ * attn_decode_paged with the arms above (arms must not be NULL; all arms off
+ * gives the plain result up to rounding). Layouts as the plain calls, with
+ * V rows [.., n_kv_heads, v_head_dim] and o [batch, n_heads, v_head_dim];
+ * the workspace is attn_decode_workspace_size(batch, n_heads, n_kv_heads,
+ * v_head_dim, max_seq_len). For the same rows and arms the two give
+ * bitwise-identical results.
+ *   Built: (PKVA_BF16, head_dim 128 or 192, v_head_dim 128),
+ *          (PKVA_F32, 16, 16); group sizes as the plain calls.
+ *   PKVA_EINVAL also for a negative window or v_head_dim, or a softcap that
+ *   is negative or not finite.
+ */
+int attn_decode_contig_ext(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                           void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                           const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                           float attention_scale, const pkva_arms* arms, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int attn_decode_paged_ext(int dtype, const void* q, const void* k_pool, const void* v_pool,
+                          void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                          const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                          int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                          float attention_scale, const pkva_arms* arms, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * attn_decode_paged_noalloc: attn_decode_paged for callers that cannot

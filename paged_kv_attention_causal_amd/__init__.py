@@ -27,6 +27,9 @@ __all__ = [
     "attn_decode_contig",
     "attn_decode_paged",
     "attn_decode_paged_noalloc",
+    "attn_decode_contig_ext",
+    "attn_decode_paged_ext",
+    "Arms",
     "attn_decode_workspace_size",
     "mla_decode_latent",
     "mla_decode_workspace_size",
@@ -42,6 +45,13 @@ BF16 = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkvattn.h")
 _LIB = None
+
+
+class Arms(ctypes.Structure):
+    """``pkva_arms``: the optional arms of one attention layer (see pkvattn.h)."""
+    _fields_ = [("window", ctypes.c_int), ("softcap", ctypes.c_float),
+                ("alibi_slopes", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+                ("v_head_dim", ctypes.c_int)]
 
 
 class PkvaError(RuntimeError):
@@ -85,6 +95,13 @@ def lib():
         L.attn_decode_paged.restype = i32
         L.attn_decode_paged.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, i32,
                                         vp, i32, f32, vp, sz, vp]
+        ap = ctypes.POINTER(Arms)
+        L.attn_decode_contig_ext.restype = i32
+        L.attn_decode_contig_ext.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32,
+                                             f32, ap, vp, sz, vp]
+        L.attn_decode_paged_ext.restype = i32
+        L.attn_decode_paged_ext.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32,
+                                            i32, vp, i32, f32, ap, vp, sz, vp]
         L.attn_decode_paged_noalloc.restype = i32
         L.attn_decode_paged_noalloc.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, vp, i32, f32, vp]
@@ -280,6 +297,67 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, max_seq_len: 
                                  _ptr(seq_lens), max_seq_len, attention_scale, _ptr(workspace),
                                  workspace.numel(), _stream(q, stream))
     _check("attn_decode_paged", st)
+    return out
+
+
+def _arms(q, v, window, softcap, alibi, sinks):
+    import torch
+    H = q.shape[1]
+    for t, n in ((alibi, "alibi"), (sinks, "sinks")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.float32 or t.numel() != H:
+                raise ValueError(f"{n} must be float32 [n_heads]")
+    return Arms(int(window), float(softcap), None if alibi is None else _ptr(alibi),
+                None if sinks is None else _ptr(sinks), int(v.shape[-1]))
+
+
+def attn_decode_contig_ext(q, k_cache, v_cache, seq_lens, *, max_seq_len: int,
+                           attention_scale: float, window: int = 0, softcap: float = 0.0,
+                           alibi=None, sinks=None, out=None, workspace=None, stream=None):
+    """:func:`attn_decode_contig` with a layer's arms; ``v_cache`` rows may be narrower
+    than ``k_cache`` rows. Returns ``[B, H, v_head_dim]``."""
+    import torch
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    _i32(seq_lens, "seq_lens")
+    B, H, D = q.shape
+    Hkv, Dv = k_cache.shape[2], v_cache.shape[3]
+    arms = _arms(q, v_cache, window, softcap, alibi, sinks)
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out")
+    workspace = _workspace(attn_decode_workspace_size(B, H, Hkv, Dv, max_seq_len), q, workspace)
+    st = lib().attn_decode_contig_ext(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(out), B, H, Hkv, D, _ptr(seq_lens), k_cache.shape[1],
+                                      max_seq_len, attention_scale, ctypes.byref(arms),
+                                      _ptr(workspace), workspace.numel(), _stream(q, stream))
+    _check("attn_decode_contig_ext", st)
+    return out
+
+
+def attn_decode_paged_ext(q, k_pool, v_pool, block_table, seq_lens, *, max_seq_len: int,
+                          attention_scale: float, window: int = 0, softcap: float = 0.0,
+                          alibi=None, sinks=None, out=None, workspace=None, stream=None):
+    """:func:`attn_decode_paged` with a layer's arms. Returns ``[B, H, v_head_dim]``."""
+    import torch
+    for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _dev(t, n)
+    _i32(block_table, "block_table")
+    _i32(seq_lens, "seq_lens")
+    B, H, D = q.shape
+    nb, bs, Hkv, Dv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], v_pool.shape[3]
+    arms = _arms(q, v_pool, window, softcap, alibi, sinks)
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(out, "out")
+    workspace = _workspace(attn_decode_workspace_size(B, H, Hkv, Dv, max_seq_len), q, workspace)
+    st = lib().attn_decode_paged_ext(_dtype_code(q), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(out), B, H, Hkv, D, _ptr(block_table),
+                                     block_table.shape[1], bs, nb, _ptr(seq_lens), max_seq_len,
+                                     attention_scale, ctypes.byref(arms), _ptr(workspace),
+                                     workspace.numel(), _stream(q, stream))
+    _check("attn_decode_paged_ext", st)
     return out
 
 

@@ -227,7 +227,8 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
                          const int32_t* block_table, int max_blocks_per_seq, int block_size,
                          int num_blocks, const int32_t* seq_lens, int kv_capacity,
                          int max_seq_len, float attention_scale, void* workspace,
-                         size_t workspace_bytes, void* stream, bool use_scratch = false) {
+                         size_t workspace_bytes, void* stream, bool use_scratch = false,
+                         const pkva_arms* arms = nullptr) {
   if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
   if (!q || !k || !v || !o || !seq_lens) return PKVA_EINVAL;
   if (batch < 1 || !heads_ok(n_heads, n_kv_heads, head_dim) || max_seq_len < 1) return PKVA_EINVAL;
@@ -242,9 +243,18 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
     if ((int64_t)batch * kv_capacity > INT_MAX) return PKVA_EINVAL;       // cache rows index in 31 bits
   }
   const bool bf16 = dtype == PKVA_BF16;
-  if (!pkva::decode_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
+  // The value width sets the lane layout and the partials (the keys may be wider).
+  int dv = head_dim;
+  if (arms) {
+    if (arms->v_head_dim < 0 || arms->window < 0) return PKVA_EINVAL;
+    if (!std::isfinite(arms->softcap) || arms->softcap < 0.0f) return PKVA_EINVAL;
+    if (arms->v_head_dim > 0) dv = arms->v_head_dim;
+    if (!pkva::decode_ext_supported(bf16, head_dim, dv)) return PKVA_EUNSUPPORTED;
+  } else {
+    if (!pkva::decode_supported(bf16, head_dim)) return PKVA_EUNSUPPORTED;
+  }
   DecodeShape sh;
-  const int rc0 = decode_shape(dtype, batch, n_heads, n_kv_heads, head_dim, max_seq_len, &sh);
+  const int rc0 = decode_shape(dtype, batch, n_heads, n_kv_heads, dv, max_seq_len, &sh);
   if (rc0 != PKVA_OK) return rc0;
   if (use_scratch) {
     // Only now a HIP call (the symbol lookup, once per device); it enqueues nothing.
@@ -262,7 +272,7 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
   p.block_table = block_table;
   const int64_t slots = (int64_t)sh.n_ranges + batch;
   p.ws_o = (float*)workspace;
-  p.ws_ml = p.ws_o + slots * n_heads * head_dim;
+  p.ws_ml = p.ws_o + slots * n_heads * dv;
   p.ws_cum = (int*)(p.ws_ml + slots * n_heads * 2);
   p.batch = batch; p.n_heads = n_heads; p.n_kv_heads = n_kv_heads;
   p.group = n_heads / n_kv_heads;
@@ -274,6 +284,16 @@ static int decode_common(int dtype, bool paged, const void* q, const void* k, co
   p.num_blocks = paged ? num_blocks : 0;
   p.kv_capacity = paged ? 0 : kv_capacity;
   p.scale_log2 = scale_log2(attention_scale);
+  if (arms) {
+    p.ext = true;
+    p.v_head_dim = dv;
+    p.window = arms->window;
+    p.scale = attention_scale;
+    p.softcap = arms->softcap;
+    p.inv_softcap = arms->softcap > 0.0f ? 1.0f / arms->softcap : 0.0f;
+    p.alibi = arms->alibi_slopes;
+    p.sinks = arms->sinks;
+  }
   const int rc = pkva::launch_decode(bf16, paged, head_dim, sh.gmax, p, (hipStream_t)stream);
   return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEunsupported ? PKVA_EUNSUPPORTED : PKVA_EHIP);
 }
@@ -297,6 +317,30 @@ int attn_decode_paged(int dtype, const void* q, const void* k_pool, const void* 
   return decode_common(dtype, true, q, k_pool, v_pool, o, batch, n_heads, n_kv_heads, head_dim,
                        block_table, max_blocks_per_seq, block_size, num_blocks, seq_lens, 0,
                        max_seq_len, attention_scale, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_contig_ext(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                           void* o, int batch, int n_heads, int n_kv_heads, int head_dim,
+                           const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                           float attention_scale, const pkva_arms* arms, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!arms) return PKVA_EINVAL;
+  return decode_common(dtype, false, q, k_cache, v_cache, o, batch, n_heads, n_kv_heads, head_dim,
+                       nullptr, 0, 0, 0, seq_lens, kv_capacity, max_seq_len, attention_scale,
+                       workspace, workspace_bytes, stream, false, arms);
+}
+
+int attn_decode_paged_ext(int dtype, const void* q, const void* k_pool, const void* v_pool, void* o,
+                          int batch, int n_heads, int n_kv_heads, int head_dim,
+                          const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                          int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                          float attention_scale, const pkva_arms* arms, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!arms) return PKVA_EINVAL;
+  return decode_common(dtype, true, q, k_pool, v_pool, o, batch, n_heads, n_kv_heads, head_dim,
+                       block_table, max_blocks_per_seq, block_size, num_blocks, seq_lens, 0,
+                       max_seq_len, attention_scale, workspace, workspace_bytes, stream, false,
+                       arms);
 }
 
 int attn_decode_paged_noalloc(int dtype, const void* q, const void* k_pool, const void* v_pool,

@@ -46,6 +46,7 @@ constexpr int kUnroll = PKVA_DECODE_UNROLL;  // tokens per batch per lane group 
 constexpr int kWavesG4 = PKVA_DECODE_WAVES_G4;  // waves per SIMD the group-of-4 kernels are built for
 constexpr int kBtWin = 1024;     // block-table entries cached in LDS per sub-piece
 constexpr float kLazy = 8.0f;    // log2 headroom before the running max is moved
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool BF16>
 struct Lane16 {
@@ -102,20 +103,47 @@ __device__ __forceinline__ int block_scan(int x, int* s_tmp) {
   return x + add;
 }
 
-__device__ __forceinline__ int valid_len(const DecodeParams& p, int b) {
+// The keys sequence b attends to: tokens start .. start + n - 1 with n its
+// valid length (0 for a length outside [1, max_seq_len]) or, with a sliding
+// window, the last `window` of them.
+template <bool EXT>
+__device__ __forceinline__ int span_len(const DecodeParams& p, int b, int* start) {
   const int L = p.seq_lens[b];
-  return (L >= 1 && L <= p.max_seq_len) ? L : 0;
+  *start = 0;
+  if (L < 1 || L > p.max_seq_len) return 0;
+  if constexpr (EXT) {
+    if (p.window > 0 && L > p.window) {
+      *start = L - p.window;
+      return p.window;
+    }
+  }
+  return L;
 }
 
-template <bool BF16, int D, int GMAX, bool PAGED, bool WIDE = false>
+// The logit of a score in the exp2 domain with the layer's arms:
+// x = scale * s, then softcap * tanh(x / softcap), plus slope * (t - pos).
+__device__ __forceinline__ float arm_logit(const DecodeParams& p, float s, float slope, int rel) {
+  float x = s * p.scale;
+  if (p.softcap > 0.0f) x = p.softcap * tanhf(x * p.inv_softcap);
+  x = fmaf(slope, (float)rel, x);
+  return x * kLog2e;
+}
+
+// EXT: the arms (window, softcap, ALiBi, sinks) and keys DX elements wider
+// than the values (K rows D + DX wide, V rows D wide). Scores then live in
+// the exp2 domain (c = 1) instead of raw dot products.
+template <bool BF16, int D, int GMAX, bool PAGED, bool WIDE = false, bool EXT = false, int DX = 0>
 __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4)) void decode_partial(DecodeParams p) {
   constexpr int E = Lane16<BF16>::E;
   constexpr int LG = D / E;          // lanes per (token, kv head) row
   constexpr int NG = kThreads / LG;  // lane groups per workgroup
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int U = GMAX >= 8 ? 2 : kUnroll;  // tokens per batch per lane group
+  constexpr int DK = D + DX;         // key width
+  constexpr int LX = DX / E;         // lanes that hold a second K chunk
   static_assert(D % E == 0 && kThreads % LG == 0 && LG <= 16 && kUnroll % 2 == 0,
                 "head size must split into at most 16 lanes of 16 bytes");
+  static_assert(DX % E == 0 && LX <= LG && (EXT || DX == 0), "extra key width");
   // Merge buffer: per (sub-row, kv head) slice GMAX*D partial sums + GMAX m and l.
   constexpr int SLICE = GMAX * D + 2 * GMAX;
 
@@ -132,7 +160,8 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
   int total = 0;
   for (int base = 0; base < p.batch; base += kThreads) {
     const int b = base + tid;
-    const int len = b < p.batch ? valid_len(p, b) : 0;
+    int st;
+    const int len = b < p.batch ? span_len<EXT>(p, b, &st) : 0;
     const int incl = block_scan(len, s_tmp);
     if (wg == 0 && slab == 0 && b < p.batch) p.ws_cum[b] = total + incl - len;
     if (tid == kThreads - 1) s_tmp[5] = incl;
@@ -152,7 +181,8 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
     int run = 0;
     for (int base = 0; base < p.batch; base += kThreads) {
       const int b = base + tid;
-      const int len = b < p.batch ? valid_len(p, b) : 0;
+      int st;
+      const int len = b < p.batch ? span_len<EXT>(p, b, &st) : 0;
       const int incl = run + block_scan(len, s_tmp);
       // the one sequence with cum_excl <= r_begin < cum_incl
       if (b < p.batch && len > 0 && incl > r_begin && incl - len <= r_begin) {
@@ -173,32 +203,46 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
   const int kvl = g % kvs, r = g / kvs;
   const int kvh = slab * kvs + kvl;
   const int HS = kvs * G;
-  const uint32_t row_bytes = (uint32_t)(p.n_kv_heads * D * ESZ);
+  const uint32_t k_row_bytes = (uint32_t)(p.n_kv_heads * DK * ESZ);
+  const uint32_t v_row_bytes = (uint32_t)(p.n_kv_heads * D * ESZ);
   const int shift = p.block_shift;
   const int bs_mask = (1 << shift) - 1;
-  const float c = p.scale_log2;
-  const char* kbase0 = (const char*)p.k + ((int64_t)kvh * D + li * E) * ESZ;
+  const float c = EXT ? 1.0f : p.scale_log2;
+  const char* kbase0 = (const char*)p.k + ((int64_t)kvh * DK + li * E) * ESZ;
+  const char* kxbase0 = kbase0 + D * ESZ;   // the lane's second K chunk (li < LX)
   const char* vbase0 = (const char*)p.v + ((int64_t)kvh * D + li * E) * ESZ;
 
   int b = s_first;
   int64_t cum = s_first_cum;
   for (; b < p.batch && cum < r_end; ++b) {
-    const int L = valid_len(p, b);
+    int start;
+    const int L = span_len<EXT>(p, b, &start);
     if (L == 0) continue;
-    const int t_lo = (int)(max<int64_t>(r_begin, cum) - cum);
-    const int t_hi = (int)(min<int64_t>(r_end, cum + L) - cum);
+    // the piece's tokens, as absolute positions in the sequence
+    const int t_lo = (int)(max<int64_t>(r_begin, cum) - cum) + start;
+    const int t_hi = (int)(min<int64_t>(r_end, cum + L) - cum) + start;
     cum += L;
     if (t_hi <= t_lo) continue;
+    const int qpos = start + L - 1;   // the query's position
 
     // This lane's slice of its group's G query rows.
-    uint4 q[GMAX];
+    uint4 q[GMAX], qx[GMAX];
+    float slope[GMAX];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
+      q[h] = make_uint4(0, 0, 0, 0);
+      qx[h] = make_uint4(0, 0, 0, 0);
+      slope[h] = 0.0f;
       if (h < G) {
-        const int64_t qoff = ((int64_t)b * p.n_heads + (int64_t)kvh * G + h) * D + li * E;
+        const int head = kvh * G + h;
+        const int64_t qoff = ((int64_t)b * p.n_heads + head) * DK + li * E;
         q[h] = *(const uint4*)((const char*)p.q + qoff * ESZ);
-      } else {
-        q[h] = make_uint4(0, 0, 0, 0);
+        if constexpr (DX > 0) {
+          if (li < LX) qx[h] = *(const uint4*)((const char*)p.q + (qoff + D) * ESZ);
+        }
+        if constexpr (EXT) {
+          if (p.alibi != nullptr) slope[h] = p.alibi[head];
+        }
       }
     }
     float acc[GMAX][E];
@@ -235,34 +279,55 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
 
       // Load the K (or V) rows of the batch starting at token t0. Rows past the
       // piece read as zero.
-      auto row_off = [&](int t) -> uint64_t {
+      auto row_of = [&](int t) -> uint64_t {
         // pool (or cache) row index; the host checks that it fits in 31 bits
-        const uint32_t row = PAGED ? (uint32_t)((s_blk[(t >> shift) - blk0] << shift) + (t & bs_mask))
-                                   : (uint32_t)(seq_row0 + t);
-        return (uint64_t)row * row_bytes;
+        return PAGED ? (uint32_t)((s_blk[(t >> shift) - blk0] << shift) + (t & bs_mask))
+                     : (uint32_t)(seq_row0 + t);
       };
-      auto load_rows = [&](uint4 (&x)[U], const char* base, int t0) {
+      auto load_rows = [&](uint4 (&x)[U], const char* base, uint32_t row_bytes, int t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int t = t0 + u * R;
           x[u] = make_uint4(0, 0, 0, 0);
-          if (t < c1) x[u] = *(const uint4*)(base + row_off(t));
+          if (t < c1) x[u] = *(const uint4*)(base + row_of(t) * row_bytes);
+        }
+      };
+      // K rows: the lane's chunk, and its second chunk when the keys are wider.
+      auto load_k = [&](uint4 (&x)[U], uint4 (&xx)[DX > 0 ? U : 1], int t0) {
+        load_rows(x, kbase0, k_row_bytes, t0);
+        if constexpr (DX > 0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int t = t0 + u * R;
+            xx[u] = make_uint4(0, 0, 0, 0);
+            if (li < LX && t < c1) xx[u] = *(const uint4*)(kxbase0 + row_of(t) * k_row_bytes);
+          }
         }
       };
       // Scores, online softmax and p * v for the batch at t0.
       // Scores, online softmax and p * v for the batch at t0; as soon as the
       // K (then V) rows of this batch are consumed, the registers are refilled
       // with the next batch's rows, so a batch is always in flight.
-      auto consume = [&](uint4 (&kx)[U], uint4 (&vx)[U], int t0) {
+      auto consume = [&](uint4 (&kx)[U], uint4 (&kx2)[DX > 0 ? U : 1], uint4 (&vx)[U], int t0) {
         const int tn = t0 + R * U;   // next batch
         float s[U][GMAX];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           dot_rows<BF16, GMAX>(q, kx[u], s[u]);
+          if constexpr (DX > 0) {
+            float s2[GMAX];
+            dot_rows<BF16, GMAX>(qx, kx2[u], s2);
+#pragma unroll
+            for (int h = 0; h < GMAX; ++h) s[u][h] += s2[h];
+          }
 #pragma unroll
           for (int h = 0; h < GMAX; ++h) s[u][h] = group_sum<LG>(s[u][h]);
+          if constexpr (EXT) {
+#pragma unroll
+            for (int h = 0; h < GMAX; ++h) s[u][h] = arm_logit(p, s[u][h], slope[h], t0 + u * R - qpos);
+          }
         }
-        load_rows(kx, kbase0, tn);
+        load_k(kx, kx2, tn);
         // Online softmax against a reference max m: rescale only when a score
         // exceeds m by more than 2^kLazy in the exp2 domain (weights stay <= 2^kLazy).
         bool grow = false;
@@ -323,12 +388,12 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
               for (int e = 0; e < E; ++e) acc[h][e] = fmaf(s[u][h], x[e], acc[h][e]);
           }
         }
-        load_rows(vx, vbase0, tn);
+        load_rows(vx, vbase0, v_row_bytes, tn);
       };
-      uint4 kx[U], vx[U];
-      load_rows(kx, kbase0, c0 + r);
-      load_rows(vx, vbase0, c0 + r);
-      for (int t0 = c0 + r; t0 < c1; t0 += R * U) consume(kx, vx, t0);
+      uint4 kx[U], kx2[DX > 0 ? U : 1], vx[U];
+      load_k(kx, kx2, c0 + r);
+      load_rows(vx, vbase0, v_row_bytes, c0 + r);
+      for (int t0 = c0 + r; t0 < c1; t0 += R * U) consume(kx, kx2, vx, t0);
       return true;
     };
     if constexpr (PAGED && WIDE) {
@@ -411,11 +476,12 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
 
 // Merge the pieces of one sequence in range order, one thread per output:
 //   o = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w,
-// computed with a running maximum. The loads of up to kCombineBatch pieces
-// are issued together, so a typical sequence costs one memory round trip.
+// computed with a running maximum (EXT: a head's sink logit joins the
+// denominator at the end, with no value). The loads of up to kCombineBatch
+// pieces are issued together, so a typical sequence costs one memory round trip.
 constexpr int kCombineBatch = 16;
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool EXT>
 __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
   constexpr int HPW = kThreads / D > 0 ? kThreads / D : 1;  // heads per workgroup
   const int hgroups = (p.n_heads + HPW - 1) / HPW;
@@ -423,9 +489,10 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
   const int h = (blockIdx.x % hgroups) * HPW + threadIdx.x / D;
   const int d = threadIdx.x % D;
   if (h >= p.n_heads) return;
-  const int L = p.seq_lens[b];
+  int start;
+  const int L = span_len<EXT>(p, b, &start);
   float out = __builtin_nanf("");
-  if (L >= 1 && L <= p.max_seq_len) {
+  if (L > 0) {
     const int per = p.ws_cum[p.batch + 1];
     const int cb = p.ws_cum[b];
     const int w0 = cb / per, w1 = (cb + L - 1) / per;
@@ -452,6 +519,15 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
         }
       }
     }
+    if constexpr (EXT) {
+      if (p.sinks != nullptr) {
+        const float sk = p.sinks[h] * kLog2e;
+        const float Mn = fmaxf(M, sk);
+        const float a = __builtin_amdgcn_exp2f(M - Mn);
+        num *= a;
+        den = den * a + __builtin_amdgcn_exp2f(sk - Mn);
+      }
+    }
     out = num / den;
   }
   const int64_t o = ((int64_t)b * p.n_heads + h) * D + d;
@@ -466,46 +542,41 @@ __global__ __launch_bounds__(kThreads) void decode_combine(DecodeParams p) {
 // device (compute units, and the resident workgroups per unit of each
 // kernel instantiation): the runtime queries cost microseconds per call.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 8;    // (bf16 D=128, fp32 D=16) x group sizes 1, 2, 4, 8
-std::atomic<int> g_slots_per_cu[kMaxDevices][kVariants];   // 0 = not looked up yet
-std::atomic<int> g_cus[kMaxDevices];
-
-template <bool BF16, int GMAX>
-constexpr int variant_index() {
-  return (BF16 ? 0 : 4) + (GMAX == 1 ? 0 : GMAX == 2 ? 1 : GMAX == 4 ? 2 : 3);
-}
+std::atomic<int> g_cus[kMaxDevices];   // 0 = not looked up yet
 
 // Token ranges for one launch: one per workgroup slot the device can keep
 // resident (compute units x workgroups per unit), never more than the
 // workspace holds or than min-size ranges the batch can fill. The slot count
 // is the smaller of the contiguous and paged kernels' occupancy, so the two
 // entry points always cut the same ranges and stay bitwise equal.
-template <bool BF16, int D, int GMAX>
+template <bool BF16, int D, int GMAX, bool EXT, int DX>
 int resident_ranges(const DecodeParams& p) {
+  static std::atomic<int> slots_per_cu[kMaxDevices];   // per instantiation; 0 = not yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
-  constexpr int vi = variant_index<BF16, GMAX>();
   int cus = g_cus[dev].load(std::memory_order_relaxed);
-  int occ = g_slots_per_cu[dev][vi].load(std::memory_order_relaxed);
+  int occ = slots_per_cu[dev].load(std::memory_order_relaxed);
   if (cus <= 0 || occ <= 0) {
     int occ_c = 0, occ_p = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_c, decode_partial<BF16, D, GMAX, false>,
-                                                     kThreads, 0) != hipSuccess) return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, decode_partial<BF16, D, GMAX, true>,
-                                                     kThreads, 0) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_c, decode_partial<BF16, D, GMAX, false, false, EXT, DX>, kThreads, 0) != hipSuccess)
+      return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ_p, decode_partial<BF16, D, GMAX, true, false, EXT, DX>, kThreads, 0) != hipSuccess)
+      return -1;
     occ = max(1, min(occ_c, occ_p));
     // Two threads may both look it up; they store the same values.
     g_cus[dev].store(cus, std::memory_order_relaxed);
-    g_slots_per_cu[dev][vi].store(occ, std::memory_order_relaxed);
+    slots_per_cu[dev].store(occ, std::memory_order_relaxed);
   }
   const int slots = cus * occ / p.nslab;
   return max(1, min(p.n_ranges, slots));
 }
 
-template <bool BF16, int D, int GMAX, bool PAGED>
+template <bool BF16, int D, int GMAX, bool PAGED, bool EXT, int DX>
 int launch_one(DecodeParams p, hipStream_t stream) {
-  p.n_ranges = resident_ranges<BF16, D, GMAX>(p);
+  p.n_ranges = resident_ranges<BF16, D, GMAX, EXT, DX>(p);
   if (p.n_ranges < 1) return kEhip;
   dim3 grid(p.n_ranges, p.nslab);
   // A piece holds at most `per` tokens, per <= max(min range, ceil(B * max_len / ranges)),
@@ -514,27 +585,35 @@ int launch_one(DecodeParams p, hipStream_t stream) {
   const int64_t per_max = by_len > p.min_tokens_per_range ? by_len : p.min_tokens_per_range;
   const bool wide = PAGED && (per_max >> p.block_shift) + 2 > kBtWin;
   if (wide) {
-    hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED, true, EXT, DX>), grid, dim3(kThreads),
+                       0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_partial<BF16, D, GMAX, PAGED, false, EXT, DX>), grid, dim3(kThreads),
+                       0, stream, p);
   }
   if (hipGetLastError() != hipSuccess) return kEhip;
   constexpr int HPW = kThreads / D > 0 ? kThreads / D : 1;
   const int cgrid = p.batch * ((p.n_heads + HPW - 1) / HPW);
-  hipLaunchKernelGGL((decode_combine<BF16, D>), dim3(cgrid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_combine<BF16, D, EXT>), dim3(cgrid), dim3(kThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return kEhip;
   return kOk;
 }
 
-template <bool BF16, int D, bool PAGED>
+template <bool BF16, int D, bool PAGED, bool EXT, int DX>
 int launch_g(const DecodeParams& p, int gmax, hipStream_t stream) {
   switch (gmax) {
-    case 1: return launch_one<BF16, D, 1, PAGED>(p, stream);
-    case 2: return launch_one<BF16, D, 2, PAGED>(p, stream);
-    case 4: return launch_one<BF16, D, 4, PAGED>(p, stream);
-    case 8: return launch_one<BF16, D, 8, PAGED>(p, stream);
+    case 1: return launch_one<BF16, D, 1, PAGED, EXT, DX>(p, stream);
+    case 2: return launch_one<BF16, D, 2, PAGED, EXT, DX>(p, stream);
+    case 4: return launch_one<BF16, D, 4, PAGED, EXT, DX>(p, stream);
+    case 8: return launch_one<BF16, D, 8, PAGED, EXT, DX>(p, stream);
     default: return kEunsupported;
   }
+}
+
+template <bool BF16, int D, bool EXT, int DX>
+int launch_p(bool paged, const DecodeParams& p, int gmax, hipStream_t stream) {
+  return paged ? launch_g<BF16, D, true, EXT, DX>(p, gmax, stream)
+               : launch_g<BF16, D, false, EXT, DX>(p, gmax, stream);
 }
 
 }  // namespace
@@ -580,18 +659,26 @@ bool decode_supported(bool bf16, int head_dim) {
   return (bf16 && head_dim == 128) || (!bf16 && head_dim == 16);
 }
 
+bool decode_ext_supported(bool bf16, int head_dim, int v_head_dim) {
+  return bf16 ? (v_head_dim == 128 && (head_dim == 128 || head_dim == 192))
+              : (head_dim == 16 && v_head_dim == 16);
+}
+
 int decode_lanes_per_row(bool bf16, int head_dim) { return head_dim / (bf16 ? 8 : 4); }
 
 int launch_decode(bool bf16, bool paged, int head_dim, int gmax, const DecodeParams& p,
                   hipStream_t stream) {
-  if (bf16 && head_dim == 128) {
-    return paged ? launch_g<true, 128, true>(p, gmax, stream)
-                 : launch_g<true, 128, false>(p, gmax, stream);
+  if (p.ext) {
+    if (bf16 && p.v_head_dim == 128 && head_dim == 128)
+      return launch_p<true, 128, true, 0>(paged, p, gmax, stream);
+    if (bf16 && p.v_head_dim == 128 && head_dim == 192)
+      return launch_p<true, 128, true, 64>(paged, p, gmax, stream);
+    if (!bf16 && head_dim == 16 && p.v_head_dim == 16)
+      return launch_p<false, 16, true, 0>(paged, p, gmax, stream);
+    return kEunsupported;
   }
-  if (!bf16 && head_dim == 16) {
-    return paged ? launch_g<false, 16, true>(p, gmax, stream)
-                 : launch_g<false, 16, false>(p, gmax, stream);
-  }
+  if (bf16 && head_dim == 128) return launch_p<true, 128, false, 0>(paged, p, gmax, stream);
+  if (!bf16 && head_dim == 16) return launch_p<false, 16, false, 0>(paged, p, gmax, stream);
   return kEunsupported;
 }
 

@@ -32,12 +32,22 @@ struct DecodeParams {
   int max_blocks_per_seq, block_shift, num_blocks;
   int kv_capacity;
   float scale_log2;           // attention_scale * log2(e)
+  // The arms of one layer (ext only): keys wider than values, sliding window,
+  // logit softcap, ALiBi slopes, sink logits.
+  bool ext;
+  int v_head_dim;             // value width (ext; the key width is head_dim)
+  int window;                 // > 0: keys within the last `window` positions
+  float scale;                // attention_scale
+  float softcap, inv_softcap; // softcap > 0: logit -> softcap * tanh(logit / softcap)
+  const float* alibi;         // [n_heads] slopes or null
+  const float* sinks;         // [n_heads] sink logits or null
 };
 
 int decode_max_ranges();
 int decode_min_tokens_per_range();
 int decode_heads_per_slab_max();
 bool decode_supported(bool bf16, int head_dim);
+bool decode_ext_supported(bool bf16, int head_dim, int v_head_dim);
 int decode_lanes_per_row(bool bf16, int head_dim);
 int launch_decode(bool bf16, bool paged, int head_dim, int gmax, const DecodeParams& p,
                   hipStream_t stream);

@@ -26,6 +26,8 @@ __all__ = [
     "bf16_round",
     "to_storage",
     "draw_block_tables",
+    "alibi_slopes",
+    "sink_logits",
     "PrefillCase",
     "DecodeCase",
     "MlaCase",
@@ -164,16 +166,17 @@ class DecodeCase:
         """
         cap = int(self.seq_lens.max()) if capacity is None else int(capacity)
         B = self.batch
-        shp = (B, cap) + self.k_pool.shape[2:]
-        kc = np.full(shp, fill, dtype=np.float32)
-        vc = np.full(shp, fill, dtype=np.float32)
+        kshp = (B, cap) + self.k_pool.shape[2:]
+        vshp = (B, cap) + self.v_pool.shape[2:]
+        kc = np.full(kshp, fill, dtype=np.float32)
+        vc = np.full(vshp, fill, dtype=np.float32)
         bs = self.block_size
         for b in range(B):
             L = int(self.seq_lens[b])
             nb = (L + bs - 1) // bs
             ids = self.block_table[b, :nb]
-            kc[b, :L] = self.k_pool[ids].reshape((nb * bs,) + shp[2:])[:L]
-            vc[b, :L] = self.v_pool[ids].reshape((nb * bs,) + shp[2:])[:L]
+            kc[b, :L] = self.k_pool[ids].reshape((nb * bs,) + kshp[2:])[:L]
+            vc[b, :L] = self.v_pool[ids].reshape((nb * bs,) + vshp[2:])[:L]
         return kc, vc
 
 
@@ -232,8 +235,11 @@ def prefill_case(seed: int = 0, *, dtype="bf16", batch=1, n_heads=28, n_kv_heads
 
 def paged_decode_case(seed: int = 0, *, dtype="bf16", batch=64, len_lo=512, len_hi=8192,
                       n_heads=32, n_kv_heads=8, head_dim=128, block_size=16, slack=0.10,
-                      max_blocks_per_seq=None, scale=None, seq_lens=None) -> DecodeCase:
-    """Paged decode: lengths uniform on ``[len_lo, len_hi]`` (both ends included)."""
+                      max_blocks_per_seq=None, scale=None, seq_lens=None,
+                      v_head_dim=None) -> DecodeCase:
+    """Paged decode: lengths uniform on ``[len_lo, len_hi]`` (both ends included).
+
+    ``v_head_dim`` (default ``head_dim``) is the width of the V rows."""
     rng = np.random.default_rng(seed)
     if seq_lens is None:
         seq_lens = rng.integers(len_lo, len_hi + 1, size=batch).astype(np.int32)
@@ -244,11 +250,21 @@ def paged_decode_case(seed: int = 0, *, dtype="bf16", batch=64, len_lo=512, len_
     num_blocks, bt = draw_block_tables(rng, seq_lens, block_size, slack, max_blocks_per_seq)
     q = _normal(rng, (batch, n_heads, head_dim), dtype)
     kp = _normal(rng, (num_blocks, block_size, n_kv_heads, head_dim), dtype)
-    vp = _normal(rng, (num_blocks, block_size, n_kv_heads, head_dim), dtype)
+    vp = _normal(rng, (num_blocks, block_size, n_kv_heads, v_head_dim or head_dim), dtype)
     if scale is None:
         scale = 1.0 / np.sqrt(head_dim)
     return DecodeCase(dtype, q, kp, vp, bt, block_size, seq_lens, n_heads, n_kv_heads,
                       head_dim, float(scale))
+
+
+def alibi_slopes(n_heads: int) -> np.ndarray:
+    """The usual ALiBi slopes for ``n_heads`` heads: ``2^(-8 (h + 1) / n_heads)``."""
+    return np.exp2(-8.0 * (np.arange(n_heads) + 1) / n_heads).astype(np.float32)
+
+
+def sink_logits(seed: int, n_heads: int, std: float = 2.0) -> np.ndarray:
+    """Per-head sink logits, N(0, std^2) in float32."""
+    return (np.random.default_rng(seed).standard_normal(n_heads) * std).astype(np.float32)
 
 
 def chunked_paged_prefill_case(seed: int = 0, *, dtype="bf16", batch=8, cached=3584, seq_q=512,

@@ -177,3 +177,119 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         pk.attn_decode_contig(q, torch.zeros(1, 8, 2, 16), torch.zeros(1, 8, 2, 16),
                               torch.ones(1, dtype=torch.int32), max_seq_len=8, attention_scale=0.25)
+
+
+# ---------------------------------------------------------------- ragged prefill, push, arms
+
+def _varlen(L, **kw):
+    a = dict(dtype=1, q=P, k=P, v=P, o=P, batch=4, n_heads=32, n_kv_heads=8, head_dim=128,
+             cu=P, skv=P, total_q=100, max_q=64, scale=0.088, bt=P, maxb=8, bs=16, nb=40, cap=0)
+    a.update(kw)
+    return L.attn_prefill_varlen(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["batch"],
+                                 a["n_heads"], a["n_kv_heads"], a["head_dim"], a["cu"], a["skv"],
+                                 a["total_q"], a["max_q"], a["scale"], a["bt"], a["maxb"], a["bs"],
+                                 a["nb"], a["cap"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), EUNSUP),
+    (dict(cu=NULL), EINVAL),
+    (dict(skv=NULL), EINVAL),
+    (dict(total_q=0), EINVAL),
+    (dict(max_q=0), EINVAL),
+    (dict(n_kv_heads=5), EINVAL),
+    (dict(scale=-1.0), EINVAL),
+    (dict(bs=12), EINVAL),
+    (dict(nb=(1 << 27)), EINVAL),              # pool rows beyond 31 bits
+    (dict(bt=NULL, cap=0), EINVAL),           # contiguous without a capacity
+    (dict(bt=NULL, batch=3, cap=(1 << 30)), EINVAL),
+    (dict(head_dim=64), EUNSUP),
+])
+def test_prefill_varlen_validation(L, kw, code):
+    assert _varlen(L, **kw) == code
+
+
+def _append(L, **kw):
+    a = dict(dtype=1, kn=P, vn=P, kc=P, vc=P, batch=2, hkv=8, d=128, n_new=1, pos=P, bt=P, maxb=4,
+             bs=16, nb=10, cap=0)
+    a.update(kw)
+    return L.kv_append(a["dtype"], a["kn"], a["vn"], a["kc"], a["vc"], a["batch"], a["hkv"], a["d"],
+                       a["n_new"], a["pos"], a["bt"], a["maxb"], a["bs"], a["nb"], a["cap"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=4), EUNSUP),
+    (dict(kn=NULL), EINVAL),
+    (dict(pos=NULL), EINVAL),
+    (dict(n_new=0), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(bs=6), EINVAL),
+    (dict(nb=0), EINVAL),
+    (dict(bt=NULL, cap=0), EINVAL),
+])
+def test_kv_append_validation(L, kw, code):
+    assert _append(L, **kw) == code
+
+
+def _mla_append(L, **kw):
+    a = dict(dtype=1, c=P, kr=P, lat=P, batch=2, R=512, Pr=64, pos=P, theta=1e4, bt=NULL, maxb=0,
+             bs=0, nb=0, cap=10)
+    a.update(kw)
+    return L.mla_append_latent(a["dtype"], a["c"], a["kr"], a["lat"], a["batch"], a["R"], a["Pr"],
+                               a["pos"], a["theta"], a["bt"], a["maxb"], a["bs"], a["nb"], a["cap"],
+                               NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), EUNSUP),
+    (dict(c=NULL), EINVAL),
+    (dict(kr=NULL), EINVAL),
+    (dict(Pr=63), EINVAL),                  # the rotary width pairs entries
+    (dict(theta=float("nan")), EINVAL),
+    (dict(cap=0), EINVAL),
+    (dict(bt=P, maxb=2, bs=3, nb=4), EINVAL),
+])
+def test_mla_append_validation(L, kw, code):
+    assert _mla_append(L, **kw) == code
+
+
+def _ext(L, paged, arms, **kw):
+    a = dict(dtype=1, q=P, k=P, v=P, o=P, batch=4, n_heads=32, n_kv_heads=8, head_dim=128,
+             bt=P, maxb=8, bs=16, nb=100, lens=P, cap=128, maxlen=128, scale=0.088,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    ap = None if arms is None else ctypes.byref(arms)
+    if paged:
+        return L.attn_decode_paged_ext(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["batch"],
+                                       a["n_heads"], a["n_kv_heads"], a["head_dim"], a["bt"],
+                                       a["maxb"], a["bs"], a["nb"], a["lens"], a["maxlen"],
+                                       a["scale"], ap, a["ws"], a["wsb"], NULL)
+    return L.attn_decode_contig_ext(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["batch"],
+                                    a["n_heads"], a["n_kv_heads"], a["head_dim"], a["lens"],
+                                    a["cap"], a["maxlen"], a["scale"], ap, a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("arms,kw,code", [
+    (None, {}, EINVAL),                                        # the arms are required
+    (pk.Arms(-1, 0.0, None, None, 0), {}, EINVAL),             # negative window
+    (pk.Arms(0, -2.0, None, None, 0), {}, EINVAL),             # negative softcap
+    (pk.Arms(0, float("inf"), None, None, 0), {}, EINVAL),
+    (pk.Arms(0, 0.0, None, None, -4), {}, EINVAL),
+    (pk.Arms(0, 0.0, None, None, 64), {}, EUNSUP),            # V width not built
+    (pk.Arms(0, 0.0, None, None, 128), dict(head_dim=256), EUNSUP),
+    (pk.Arms(8, 1.0, None, None, 128), dict(ws=NULL), EWS),
+])
+def test_decode_ext_validation(L, paged, arms, kw, code):
+    assert _ext(L, paged, arms, **kw) == code
+
+
+def test_noalloc_validation_before_any_hip_call(L):
+    # pure argument errors come back before the scratch lookup
+    assert L.attn_decode_paged_noalloc(1, P, P, P, P, 4, 32, 5, 128, P, 8, 16, 100, P, 128, 0.1,
+                                       NULL) == EINVAL
+    assert L.attn_decode_paged_noalloc(1, P, P, P, P, 4, 32, 8, 128, NULL, 8, 16, 100, P, 128, 0.1,
+                                       NULL) == EINVAL
+    # sizes beyond the 64 MiB scratch: (2048 + 4096) x 32 x 130 x 4 B
+    assert L.attn_decode_paged_noalloc(1, P, P, P, P, 4096, 32, 8, 128, P, 512, 16, 1000, P, 8192,
+                                       0.1, NULL) == 5
