@@ -48,6 +48,8 @@ __all__ = [
     "decode_paged",
     "mla_decode_latent",
     "mla_naive",
+    "mla_absorb_q",
+    "mla_up_proj",
     "mla_absorbed",
     "prefill_varlen",
     "gqa_attention_arms",
@@ -351,23 +353,48 @@ def mla_naive(q, c, k_rot, w_uk, w_uv, scale):
     return gqa_attention(q[None], keys, vals, H, H, L - 1, scale)[0]
 
 
+def mla_absorb_q(q, k_b):
+    """The absorbed query: ``q_abs[.., h] = [k_b[h] @ q_nope[.., h] | q_rot[.., h]]``.
+
+    ``q`` is ``[..., H, qk_nope + qk_rope]`` (nope part first), ``k_b`` is
+    ``[H, R, qk_nope]``, one matrix per head in the absorb direction
+    (frink-models 0.31.0 ``src/mla/mod.rs``: the ``MlaKvB::Split`` doc, and
+    ``absorbed_attention``, which applies ``k_b[h]`` to the nope part and
+    copies the rope part after it). Returns ``[..., H, R + qk_rope]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_b = np.asarray(k_b, dtype=np.float64)
+    nope = k_b.shape[2]
+    absorbed = np.einsum("hrn,...hn->...hr", k_b, q[..., :nope])
+    return np.concatenate([absorbed, q[..., nope:]], axis=-1)
+
+
+def mla_up_proj(o_lat, v_b):
+    """The per-head value up-projection: ``out[.., h] = v_b[h] @ o_lat[.., h]``.
+
+    ``o_lat`` is ``[..., H, R]``, ``v_b`` is ``[H, v_head_dim, R]``
+    (``MlaKvB::Split`` doc; the last loop of ``absorbed_attention``).
+    Returns ``[..., H, v_head_dim]``.
+    """
+    return np.einsum("hvr,...hr->...hv", np.asarray(v_b, dtype=np.float64),
+                     np.asarray(o_lat, dtype=np.float64))
+
+
 def mla_absorbed(q, c, k_rot, w_uk, w_uv, scale):
     """The absorbed MLA form of :func:`mla_naive`: same result, latent-sized cache.
 
-    The query's nope part is pulled through ``w_uk[h]^T`` into latent space,
-    attention runs over the cached latent rows ``[c_t | k_rot_t]`` with the
-    first ``R`` entries as the value, and the weighted latent is pulled up
-    through ``w_uv[h]`` (frink-models 0.31.0 ``src/mla/mod.rs``,
+    The query's nope part is pulled through ``k_b[h] = w_uk[h]^T`` into latent
+    space, attention runs over the cached latent rows ``[c_t | k_rot_t]`` with
+    the first ``R`` entries as the value, and the weighted latent is pulled up
+    through ``v_b[h] = w_uv[h]`` (frink-models 0.31.0 ``src/mla/mod.rs``,
     ``absorbed_attention``; the ``MlaKvB`` doc says the two forms compute
     the same attention).
     """
-    H = q.shape[0]
-    qk_nope = w_uk.shape[1]
     R = c.shape[1]
-    q_abs = np.concatenate([np.einsum("hnr,hn->hr", w_uk, q[:, :qk_nope]), q[:, qk_nope:]], axis=1)
+    q_abs = mla_absorb_q(q, np.transpose(w_uk, (0, 2, 1)))
     latent = np.concatenate([c, k_rot], axis=1)
     o_lat = mla_decode_latent(q_abs[None], latent[None], [c.shape[0]], R, scale)[0]
-    return np.einsum("hvr,hr->hv", w_uv, o_lat)
+    return mla_up_proj(o_lat, w_uv)
 
 
 # ------------------------------------------------------------------ cache append (push)

@@ -566,3 +566,29 @@ def test_arms_match_the_scalar_brute_force():
         got = O.gqa_attention_arms(q, k, v, H, Hkv, off, 0.6, **kw)
         ref = brute.gqa_attention_arms(q.tolist(), k.tolist(), v.tolist(), H, Hkv, off, 0.6, **kw)
         np.testing.assert_allclose(got, np.array(ref), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- MLA projections
+
+def test_mla_projection_closed_forms():
+    rng = np.random.default_rng(14)
+    B, H, nope, P, R, vd = 2, 3, 4, 2, 5, 3
+    q = rng.standard_normal((B, H, nope + P))
+    # k_b[h] = e_{r, n}: q_abs[.., r] picks q_nope[n]; the rope part is copied
+    k_b = np.zeros((H, R, nope))
+    for h in range(H):
+        k_b[h, (h + 1) % R, h % nope] = 2.0
+    qa = O.mla_absorb_q(q, k_b)
+    assert qa.shape == (B, H, R + P)
+    for h in range(H):
+        expect = np.zeros((B, R))
+        expect[:, (h + 1) % R] = 2.0 * q[:, h, h % nope]
+        np.testing.assert_array_equal(qa[:, h, :R], expect)
+    np.testing.assert_array_equal(qa[..., R:], q[..., nope:])
+    # up-projection by a per-head diagonal scales each latent entry
+    o = rng.standard_normal((B, H, R))
+    v_b = np.zeros((H, vd, R))
+    for h in range(H):
+        for i in range(vd):
+            v_b[h, i, i] = h + 1.0
+    np.testing.assert_array_equal(O.mla_up_proj(o, v_b), o[..., :vd] * (np.arange(H) + 1.0)[:, None])
