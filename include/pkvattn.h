@@ -9,6 +9,8 @@
  *   attn_decode_*_ext   the same with a layer's arms (window, softcap, ALiBi,
  *                       sinks, V width)
  *   mla_decode_latent   absorbed multi-head latent attention decode
+ *   mla_decode_latent_paged   the same over a paged latent pool
+ *   mla_absorb_q, mla_up_proj the per-head projections around it
  *   kv_append           push of new K/V rows into a cache or pool
  *   mla_append_latent   push of an MLA latent row, k_rot rotated once
  *
@@ -281,6 +283,56 @@ int attn_decode_paged_noalloc(int dtype, const void* q, const void* k_pool, cons
                               const int32_t* block_table, int max_blocks_per_seq, int block_size,
                               int num_blocks, const int32_t* seq_lens, int max_seq_len,
                               float attention_scale, void* stream);
+
+/*
+ * mla_decode_latent_paged: mla_decode_latent over a block-table paged latent
+ * pool (the latent cache of frink-models 0.31.0 src/mla/mod.rs,
+ * MlaKvB::Split, "[seq, kv_lora_rank + qk_rope]", laid out in pages as the
+ * K/V pools of attn_decode_paged).
+ *
+ *   latent_pool [num_blocks, block_size, kv_lora_rank + qk_rope_head_dim];
+ *   block_table [batch, max_blocks_per_seq] int32 device; token t of
+ *   sequence b is row t % block_size of block block_table[b][t / block_size].
+ *   block_size a power of two; max_seq_len <= max_blocks_per_seq *
+ *   block_size. A sequence with a needed block id outside [0, num_blocks)
+ *   gets NaN rows. Other arguments, workspace and results as
+ *   mla_decode_latent (bitwise equal for the same rows).
+ */
+int mla_decode_latent_paged(int dtype, const void* q_abs, const void* latent_pool, void* o_lat,
+                            int batch, int n_heads, int kv_lora_rank, int qk_rope_head_dim,
+                            const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                            int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                            float attention_scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * mla_absorb_q: the absorbed query of frink-models 0.31.0 src/mla/mod.rs,
+ * absorbed_attention: q_abs[b, h] = [k_b[h] . q_nope[b, h] | q_rot[b, h]],
+ * with one weight matrix per head in the absorb direction (MlaKvB::Split
+ * doc: k_b[h] is [kv_lora_rank, qk_nope]).
+ *   q      [batch, n_heads, qk_nope_head_dim + qk_rope_head_dim] (nope first)
+ *   k_b    [n_heads, kv_lora_rank, qk_nope_head_dim]
+ *   q_abs  [batch, n_heads, kv_lora_rank + qk_rope_head_dim] (written)
+ *   bf16 only, fp32 accumulation, output rounded to nearest even. Built for
+ *   qk_nope_head_dim % 16 == 0, kv_lora_rank % 32 == 0,
+ *   qk_rope_head_dim % 8 == 0 (else PKVA_EUNSUPPORTED); pointers 16-byte
+ *   aligned (else PKVA_EINVAL).
+ */
+int mla_absorb_q(int dtype, const void* q, const void* k_b, void* q_abs, int batch, int n_heads,
+                 int qk_nope_head_dim, int qk_rope_head_dim, int kv_lora_rank, void* stream);
+
+/*
+ * mla_up_proj: the per-head value up-projection after the latent attention
+ * (absorbed_attention's last loop): out[b, h] = v_b[h] . o_lat[b, h], with
+ * v_b[h] [v_head_dim, kv_lora_rank] (MlaKvB::Split doc).
+ *   o_lat  [batch, n_heads, kv_lora_rank]
+ *   v_b    [n_heads, v_head_dim, kv_lora_rank]
+ *   out    [batch, n_heads, v_head_dim] (written)
+ *   bf16 only, fp32 accumulation. Built for kv_lora_rank % 16 == 0,
+ *   v_head_dim % 32 == 0; pointers 16-byte aligned.
+ */
+int mla_up_proj(int dtype, const void* o_lat, const void* v_b, void* out, int batch, int n_heads,
+                int kv_lora_rank, int v_head_dim, void* stream);
 
 /*
  * kv_append: the push of push-then-attend. Writes n_new K and V rows per

@@ -33,6 +33,9 @@ __all__ = [
     "attn_decode_workspace_size",
     "mla_decode_latent",
     "mla_decode_workspace_size",
+    "mla_decode_latent_paged",
+    "mla_absorb_q",
+    "mla_up_proj",
     "kv_append",
     "mla_append_latent",
     "status_string",
@@ -105,6 +108,13 @@ def lib():
         L.attn_decode_paged_noalloc.restype = i32
         L.attn_decode_paged_noalloc.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                                 i32, i32, vp, i32, f32, vp]
+        L.mla_decode_latent_paged.restype = i32
+        L.mla_decode_latent_paged.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32,
+                                              i32, vp, i32, f32, vp, sz, vp]
+        L.mla_absorb_q.restype = i32
+        L.mla_absorb_q.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.mla_up_proj.restype = i32
+        L.mla_up_proj.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp]
         L.kv_append.restype = i32
         L.kv_append.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32,
                                 i32, vp]
@@ -405,6 +415,64 @@ def mla_decode_latent(q_abs, latent, seq_lens, *, kv_lora_rank: int, max_seq_len
                                  attention_scale, _ptr(workspace), workspace.numel(),
                                  _stream(q_abs, stream))
     _check("mla_decode_latent", st)
+    return out
+
+
+def mla_decode_latent_paged(q_abs, latent_pool, block_table, seq_lens, *, kv_lora_rank: int,
+                            max_seq_len: int, attention_scale: float, out=None, workspace=None,
+                            stream=None):
+    """:func:`mla_decode_latent` over a pool ``[num_blocks, block_size, R + P]``."""
+    import torch
+    _dev(q_abs, "q_abs")
+    _dev(latent_pool, "latent_pool")
+    _i32(block_table, "block_table")
+    _i32(seq_lens, "seq_lens")
+    B, H, W = q_abs.shape
+    P = W - kv_lora_rank
+    if out is None:
+        out = torch.empty((B, H, kv_lora_rank), dtype=q_abs.dtype, device=q_abs.device)
+    _dev(out, "out")
+    workspace = _workspace(mla_decode_workspace_size(B, H, kv_lora_rank, max_seq_len), q_abs,
+                           workspace)
+    st = lib().mla_decode_latent_paged(_dtype_code(q_abs), _ptr(q_abs), _ptr(latent_pool),
+                                       _ptr(out), B, H, kv_lora_rank, P, _ptr(block_table),
+                                       block_table.shape[1], latent_pool.shape[1],
+                                       latent_pool.shape[0], _ptr(seq_lens), max_seq_len,
+                                       attention_scale, _ptr(workspace), workspace.numel(),
+                                       _stream(q_abs, stream))
+    _check("mla_decode_latent_paged", st)
+    return out
+
+
+def mla_absorb_q(q, k_b, *, out=None, stream=None):
+    """``q`` ``[B, H, nope + P]``, ``k_b`` ``[H, R, nope]`` -> ``q_abs`` ``[B, H, R + P]``."""
+    import torch
+    _dev(q, "q")
+    _dev(k_b, "k_b")
+    B, H, W = q.shape
+    _, R, nope = k_b.shape
+    if out is None:
+        out = torch.empty((B, H, R + W - nope), dtype=q.dtype, device=q.device)
+    _dev(out, "out")
+    st = lib().mla_absorb_q(_dtype_code(q), _ptr(q), _ptr(k_b), _ptr(out), B, H, nope, W - nope, R,
+                            _stream(q, stream))
+    _check("mla_absorb_q", st)
+    return out
+
+
+def mla_up_proj(o_lat, v_b, *, out=None, stream=None):
+    """``o_lat`` ``[B, H, R]``, ``v_b`` ``[H, v_dim, R]`` -> ``[B, H, v_dim]``."""
+    import torch
+    _dev(o_lat, "o_lat")
+    _dev(v_b, "v_b")
+    B, H, R = o_lat.shape
+    vd = v_b.shape[1]
+    if out is None:
+        out = torch.empty((B, H, vd), dtype=o_lat.dtype, device=o_lat.device)
+    _dev(out, "out")
+    st = lib().mla_up_proj(_dtype_code(o_lat), _ptr(o_lat), _ptr(v_b), _ptr(out), B, H, R, vd,
+                           _stream(o_lat, stream))
+    _check("mla_up_proj", st)
     return out
 
 

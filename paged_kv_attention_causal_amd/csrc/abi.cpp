@@ -411,21 +411,72 @@ int mla_append_latent(int dtype, const void* c_new, const void* k_rot_new, void*
   return rc == pkva::kOk ? PKVA_OK : PKVA_EHIP;
 }
 
+int mla_absorb_q(int dtype, const void* q, const void* k_b, void* q_abs, int batch, int n_heads,
+                 int qk_nope_head_dim, int qk_rope_head_dim, int kv_lora_rank, void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!q || !k_b || !q_abs) return PKVA_EINVAL;
+  if (batch < 1 || n_heads < 1 || qk_nope_head_dim < 1 || qk_rope_head_dim < 0 ||
+      kv_lora_rank < 1)
+    return PKVA_EINVAL;
+  // bf16, 16-byte rows pieces: k steps of 16, outputs in tiles of 32, the rope
+  // part in 16-byte chunks.
+  if (dtype != PKVA_BF16 || qk_nope_head_dim % 16 != 0 || kv_lora_rank % 32 != 0 ||
+      qk_rope_head_dim % 8 != 0)
+    return PKVA_EUNSUPPORTED;
+  if ((((uintptr_t)q | (uintptr_t)k_b | (uintptr_t)q_abs) & 15u) != 0) return PKVA_EINVAL;
+  pkva::MlaProjParams p{};
+  p.x = q; p.w = k_b; p.y = q_abs;
+  p.batch = batch; p.n_heads = n_heads; p.n = kv_lora_rank; p.k = qk_nope_head_dim;
+  const int64_t qw = qk_nope_head_dim + qk_rope_head_dim, aw = kv_lora_rank + qk_rope_head_dim;
+  p.x_stride_b = n_heads * qw; p.x_stride_h = qw;
+  p.y_stride_b = n_heads * aw; p.y_stride_h = aw;
+  p.copy_len = qk_rope_head_dim; p.copy_src = qk_nope_head_dim;
+  const int rc = pkva::launch_mla_proj(p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEinval ? PKVA_EINVAL : PKVA_EHIP);
+}
+
+int mla_up_proj(int dtype, const void* o_lat, const void* v_b, void* out, int batch, int n_heads,
+                int kv_lora_rank, int v_head_dim, void* stream) {
+  if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
+  if (!o_lat || !v_b || !out) return PKVA_EINVAL;
+  if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || v_head_dim < 1) return PKVA_EINVAL;
+  if (dtype != PKVA_BF16 || kv_lora_rank % 16 != 0 || v_head_dim % 32 != 0)
+    return PKVA_EUNSUPPORTED;
+  if ((((uintptr_t)o_lat | (uintptr_t)v_b | (uintptr_t)out) & 15u) != 0) return PKVA_EINVAL;
+  pkva::MlaProjParams p{};
+  p.x = o_lat; p.w = v_b; p.y = out;
+  p.batch = batch; p.n_heads = n_heads; p.n = v_head_dim; p.k = kv_lora_rank;
+  p.x_stride_b = (int64_t)n_heads * kv_lora_rank; p.x_stride_h = kv_lora_rank;
+  p.y_stride_b = (int64_t)n_heads * v_head_dim; p.y_stride_h = v_head_dim;
+  p.copy_len = 0; p.copy_src = 0;
+  const int rc = pkva::launch_mla_proj(p, (hipStream_t)stream);
+  return rc == pkva::kOk ? PKVA_OK : (rc == pkva::kEinval ? PKVA_EINVAL : PKVA_EHIP);
+}
+
 size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seq_len) {
   if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || max_seq_len < 1) return 0;
   if (!pkva::mla_supported(true, kv_lora_rank, 64, n_heads)) return 0;
   return mla_shape(batch, n_heads, kv_lora_rank, max_seq_len).ws_bytes;
 }
 
-int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_lat, int batch,
+static int mla_common(int dtype, const void* q_abs, const void* latent, void* o_lat, int batch,
                       int n_heads, int kv_lora_rank, int qk_rope_head_dim,
-                      const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                      const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                      int num_blocks, const int32_t* seq_lens, int kv_capacity, int max_seq_len,
                       float attention_scale, void* workspace, size_t workspace_bytes,
                       void* stream) {
   if (!dtype_known(dtype)) return PKVA_EUNSUPPORTED;
   if (!q_abs || !latent || !o_lat || !seq_lens) return PKVA_EINVAL;
   if (batch < 1 || n_heads < 1 || kv_lora_rank < 1 || qk_rope_head_dim < 0) return PKVA_EINVAL;
-  if (max_seq_len < 1 || kv_capacity < max_seq_len) return PKVA_EINVAL;
+  if (max_seq_len < 1) return PKVA_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (!is_pow2(block_size) || max_blocks_per_seq < 1 || num_blocks < 1) return PKVA_EINVAL;
+    if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKVA_EINVAL;
+    if ((int64_t)num_blocks * block_size > INT_MAX) return PKVA_EINVAL;   // pool rows index in 31 bits
+  } else {
+    if (kv_capacity < max_seq_len) return PKVA_EINVAL;
+  }
   if (!scale_ok(attention_scale)) return PKVA_EINVAL;
   if (!pkva::mla_supported(dtype == PKVA_BF16, kv_lora_rank, qk_rope_head_dim, n_heads))
     return PKVA_EUNSUPPORTED;
@@ -442,11 +493,38 @@ int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_
   p.ws_o = (__bf16*)workspace;
   p.ws_ml = sh.ws_bytes > 0 ? (float*)(p.ws_o + (int64_t)batch * sh.nsplit * n_heads * kv_lora_rank)
                             : nullptr;
-  p.batch = batch; p.n_heads = n_heads; p.kv_capacity = kv_capacity; p.max_seq_len = max_seq_len;
+  p.batch = batch; p.n_heads = n_heads; p.kv_capacity = paged ? 0 : kv_capacity;
+  p.max_seq_len = max_seq_len;
   p.nsplit = sh.nsplit; p.split_tokens = sh.split_tokens;
   p.scale_log2 = scale_log2(attention_scale);
+  p.block_table = block_table;
+  p.max_blocks_per_seq = paged ? max_blocks_per_seq : 0;
+  p.block_shift = paged ? log2i(block_size) : 0;
+  p.num_blocks = paged ? num_blocks : 0;
   const int rc = pkva::launch_mla(p, (hipStream_t)stream);
   return rc == pkva::kOk ? PKVA_OK : PKVA_EHIP;
+}
+
+int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_lat, int batch,
+                      int n_heads, int kv_lora_rank, int qk_rope_head_dim,
+                      const int32_t* seq_lens, int kv_capacity, int max_seq_len,
+                      float attention_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return mla_common(dtype, q_abs, latent, o_lat, batch, n_heads, kv_lora_rank, qk_rope_head_dim,
+                    nullptr, 0, 0, 0, seq_lens, kv_capacity, max_seq_len, attention_scale,
+                    workspace, workspace_bytes, stream);
+}
+
+int mla_decode_latent_paged(int dtype, const void* q_abs, const void* latent_pool, void* o_lat,
+                            int batch, int n_heads, int kv_lora_rank, int qk_rope_head_dim,
+                            const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                            int num_blocks, const int32_t* seq_lens, int max_seq_len,
+                            float attention_scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!block_table) return PKVA_EINVAL;
+  return mla_common(dtype, q_abs, latent_pool, o_lat, batch, n_heads, kv_lora_rank,
+                    qk_rope_head_dim, block_table, max_blocks_per_seq, block_size, num_blocks,
+                    seq_lens, 0, max_seq_len, attention_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 OUT = os.path.join(PKG, "libpkvattn.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["abi.cpp", "decode.hip", "prefill.hip", "mla.hip", "append.hip"]
+SOURCES = ["abi.cpp", "decode.hip", "prefill.hip", "mla.hip", "append.hip", "mla_proj.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no packed fp32 VALU ops in device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

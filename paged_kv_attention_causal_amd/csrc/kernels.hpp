@@ -88,6 +88,9 @@ struct MlaParams {
   int batch, n_heads, kv_capacity, max_seq_len;
   int nsplit, split_tokens;   // context split: nsplit pieces of split_tokens tokens
   float scale_log2;
+  // Paged latent (null block_table: contiguous [batch, kv_capacity, R + P]):
+  const int32_t* block_table; // [batch, max_blocks_per_seq]; latent is [num_blocks, bs, R + P]
+  int max_blocks_per_seq, block_shift, num_blocks;
 };
 
 bool mla_supported(bool bf16, int kv_lora_rank, int rope_dim, int n_heads);
@@ -116,6 +119,20 @@ struct MlaAppendParams {
   int kv_lora_rank, rope_dim;
   double theta;               // <= 0: no rotation
 };
+
+// Batched per-head GEMM Y[b, h, :n] = W[h] (n x k) X[b, h, :k], bf16 in and
+// out, fp32 accumulation; optionally copies copy_len elements of each X row
+// (from element copy_src) to Y after the n outputs.
+struct MlaProjParams {
+  const void* x;              // X rows: element (b, h, i) at b * x_stride_b + h * x_stride_h + i
+  const void* w;              // [n_heads, n, k]
+  void* y;                    // element (b, h, j) at b * y_stride_b + h * y_stride_h + j
+  int batch, n_heads, n, k;
+  int64_t x_stride_b, x_stride_h, y_stride_b, y_stride_h;
+  int copy_len, copy_src;
+};
+
+int launch_mla_proj(const MlaProjParams& p, hipStream_t stream);
 
 int launch_kv_append(const AppendParams& p, hipStream_t stream);
 int launch_mla_append(const MlaAppendParams& p, bool bf16, hipStream_t stream);

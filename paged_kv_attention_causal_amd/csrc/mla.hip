@@ -53,6 +53,7 @@ constexpr int kDB = kR / 32;      // 32-row blocks of O^T (16)
 constexpr float kLazy = 8.0f;
 constexpr int kXcds = 8;          // accelerator complex dies, each with its own L2
 constexpr int kAhead = 4;        // MFMA pairs whose operands are read ahead
+constexpr int kBtWin = 512;       // block ids of a paged latent held in LDS
 static_assert(kTileB % 1024 == 0 && kChunks % 8 == 0, "tile geometry");
 static_assert(kKSteps >= 2 * kDB, "value MFMAs interleave with the score MFMAs");
 
@@ -110,11 +111,18 @@ __device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kDB], float alpha) {
   asm volatile("s_nop 7" ::: "memory");
 }
 
-template <int NW>
+// PAGED: the latent rows live in a pool [num_blocks, block_size, R + P];
+// token t of sequence b is row t % block_size of block
+// block_table[b][t / block_size]. The block ids a piece needs are checked
+// up front and held in an LDS window (reloaded, between barriers, when a
+// tile's blocks run past it); every copy then takes its row's address.
+template <int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   static_assert(kDmaTile % NW == 0, "every thread copies the same number of chunks");
   constexpr int kDmaPerThread = kDmaTile / NW;
   __shared__ __attribute__((aligned(1024))) char s_lat[kStages * kTileB];
+  __shared__ int s_bt[PAGED ? kBtWin : 1];
+  __shared__ int s_bad;
 
   // Work item = (sequence, head group, split), split fastest. Workgroups go
   // to the 8 XCDs round robin (XCD = id % 8); a run of consecutive items
@@ -133,11 +141,40 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   const int head = (hg * NW + wave) * kHW + lr;
 
   const int L = p.seq_lens[b];
-  const bool bad = L < 1 || L > p.max_seq_len;
+  bool bad = L < 1 || L > p.max_seq_len;
   const int t_begin = split * p.split_tokens;
-  const int t_end = bad ? 0 : min(L, t_begin + p.split_tokens);
+  int t_end = bad ? 0 : min(L, t_begin + p.split_tokens);
+  const char* lat = (const char*)p.latent + (PAGED ? 0 : (int64_t)b * p.kv_capacity * kRowB);
+
+  // Paged: check every block id the piece needs, then fill the window.
+  const int shift = p.block_shift;
+  const int32_t* bt_row = PAGED ? p.block_table + (int64_t)b * p.max_blocks_per_seq : nullptr;
+  int win0 = 0, win_end = 0;   // block ids [win0, win_end) of the sequence held in s_bt
+  auto load_window = [&](int blk) {
+    __syncthreads();   // no wave still reads the old window
+    win0 = blk;
+    win_end = min(blk + kBtWin, ((t_end - 1) >> shift) + 1);
+    for (int i = tid; i < win_end - win0; i += 64 * NW) s_bt[i] = bt_row[win0 + i];
+    __syncthreads();
+  };
+  if constexpr (PAGED) {
+    if (t_end > t_begin) {
+      if (tid == 0) s_bad = 0;
+      __syncthreads();
+      for (int i = (t_begin >> shift) + tid; i <= ((t_end - 1) >> shift); i += 64 * NW) {
+        const int id = bt_row[i];
+        if (id < 0 || id >= p.num_blocks) s_bad = 1;
+      }
+      __syncthreads();
+      if (s_bad) {   // a needed block lies outside the pool: NaN for the sequence
+        bad = true;
+        t_end = 0;
+      } else {
+        load_window(t_begin >> shift);
+      }
+    }
+  }
   const int n_t = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-  const char* lat = (const char*)p.latent + (int64_t)b * p.kv_capacity * kRowB;
 
   // Copy tile i (tokens t_begin + 32 i ..) into its stage. DMA op j of this
   // wave covers bytes [1024 ins, +1024) of the tile, ins = wave + NW * j,
@@ -158,6 +195,20 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(s_lat) +
                         (uint32_t)((i % kStages) * kTileB);
     const int t0 = t_begin + kTile * i;
+    if constexpr (PAGED) {
+      const int last = min(t_end - 1 - t0, kTile - 1);   // last live row of the tile
+      if (((t0 + last) >> shift) >= win_end) load_window(t0 >> shift);   // uniform
+      const int bs_mask = (1 << shift) - 1;
+#pragma unroll
+      for (int j = 0; j < kDmaPerThread; ++j) {
+        const int row = (int)(dma_off[j] / kRowB);
+        const uint32_t chunk = dma_off[j] - (uint32_t)(row * kRowB);
+        const int t = t0 + min(row, last);
+        const uint32_t prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
+        dma16_addr(lat + (uint64_t)prow * kRowB + chunk, st + 1024u * (wave + NW * j));
+      }
+      return;
+    }
     const char* base = lat + (int64_t)t0 * kRowB;
     if (t0 + kTile <= t_end) {
 #pragma unroll
@@ -379,12 +430,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     // Partial of this split: O / l in bf16 (half the traffic of the fp32
     // numerator, one more rounding of the size of the output's own), then
     // m in the log2 domain and l in fp32.
+    // A piece with a block outside the pool leaves a NaN sum, which makes
+    // the merged row NaN.
     inv = n_t > 0 ? 1.0f / l_tot : 0.0f;
     const int64_t w = ((int64_t)b * p.nsplit + split) * p.n_heads + head;
     dst = p.ws_o + (((int64_t)b * p.nsplit + split) * p.n_heads + hg * kHW * NW) * kR;
     if (hf == 0) {
       store_nt(p.ws_ml + w * 2 + 0, n_t > 0 ? m_ref * c : -INFINITY);
-      store_nt(p.ws_ml + w * 2 + 1, n_t > 0 ? l_tot : 0.0f);
+      store_nt(p.ws_ml + w * 2 + 1, n_t > 0 ? l_tot : (bad ? __builtin_nanf("") : 0.0f));
     }
   }
   constexpr int kOutRow = kR * 2 + 8;
@@ -445,7 +498,11 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine(MlaParams p) {
 template <int NW>
 int launch_nw(const MlaParams& p, hipStream_t stream) {
   const int n_items = p.batch * (p.n_heads / (kHW * NW)) * p.nsplit;
-  hipLaunchKernelGGL(mla_kernel<NW>, dim3(n_items), dim3(64 * NW), 0, stream, p);
+  if (p.block_table != nullptr) {
+    hipLaunchKernelGGL((mla_kernel<NW, true>), dim3(n_items), dim3(64 * NW), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((mla_kernel<NW, false>), dim3(n_items), dim3(64 * NW), 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? kOk : kEhip;
 }
 

@@ -36,6 +36,8 @@ __all__ = [
     "paged_decode_case",
     "chunked_paged_prefill_case",
     "mla_case",
+    "MlaProjCase",
+    "mla_proj_case",
     "VarlenPrefillCase",
     "varlen_prefill_case",
     "AppendCase",
@@ -324,6 +326,29 @@ def _history_rows(bt, held, num_blocks, block_size):
 
 
 @dataclass
+class MlaProjCase:
+    """The MLA projections' operands: ``q`` ``[B, H, nope + P]`` (nope first),
+    ``k_b`` ``[H, R, nope]`` (absorb direction), ``v_b`` ``[H, v_dim, R]``, and an
+    ``o_lat`` ``[B, H, R]`` to up-project on its own."""
+    dtype: str
+    q: np.ndarray
+    k_b: np.ndarray
+    v_b: np.ndarray
+    o_lat: np.ndarray
+
+
+def mla_proj_case(seed: int = 0, *, dtype="bf16", batch=32, n_heads=128, qk_nope=128,
+                  qk_rope=64, kv_lora_rank=512, v_head_dim=128) -> MlaProjCase:
+    """Weights N(0, 1/fan_in) (so outputs keep the inputs' scale), q and o_lat N(0,1)."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (batch, n_heads, qk_nope + qk_rope), dtype)
+    k_b = _normal(rng, (n_heads, kv_lora_rank, qk_nope), dtype, qk_nope ** -0.5)
+    v_b = _normal(rng, (n_heads, v_head_dim, kv_lora_rank), dtype, kv_lora_rank ** -0.5)
+    o_lat = _normal(rng, (batch, n_heads, kv_lora_rank), dtype)
+    return MlaProjCase(dtype, q, k_b, v_b, o_lat)
+
+
+@dataclass
 class VarlenPrefillCase:
     """A ragged batch of prefill chunks over one shared cache.
 
@@ -502,6 +527,8 @@ CONFIG_DESCRIPTIONS = {
     "varlen_prefill_paged_bf16": "ragged chunked prefill bf16 over one paged pool: 16 seqs, chunk "
                                  "U[1,1024] after U[0,4096] cached, H=32 Hkv=8 D=128 block 16, "
                                  "scale 1/sqrt(128), N(0,1)",
+    "mla_proj_bf16": "MLA absorb q_nope.k_b[h] and up-projection v_b[h].o_lat, bf16, 32 seqs, "
+                     "H=128, qk_nope 128, rope 64, R 512, v_head_dim 128, weights N(0,1/fan_in)",
     "append_paged_bf16": "push of this step's K/V row into the paged-decode pool: 64 seqs holding "
                          "511..8191 rows, Hkv=8 D=128 block 16",
     "mla_append_bf16": "push of the 4096th latent row [c | rope(k_rot)] for 32 seqs, R=512 P=64, "

@@ -293,3 +293,49 @@ def test_noalloc_validation_before_any_hip_call(L):
     # sizes beyond the 64 MiB scratch: (2048 + 4096) x 32 x 130 x 4 B
     assert L.attn_decode_paged_noalloc(1, P, P, P, P, 4096, 32, 8, 128, P, 512, 16, 1000, P, 8192,
                                        0.1, NULL) == 5
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), EUNSUP),               # bf16 only
+    (dict(q=NULL), EINVAL),
+    (dict(nope=120), EUNSUP),
+    (dict(R=500), EUNSUP),
+    (dict(Pr=6), EUNSUP),
+    (dict(batch=0), EINVAL),
+    (dict(q=ctypes.c_void_p(4104)), EINVAL),   # not 16-byte aligned
+])
+def test_mla_absorb_validation(L, kw, code):
+    a = dict(dtype=1, q=P, kb=P, qa=P, batch=4, H=16, nope=128, Pr=64, R=512)
+    a.update(kw)
+    assert L.mla_absorb_q(a["dtype"], a["q"], a["kb"], a["qa"], a["batch"], a["H"], a["nope"],
+                          a["Pr"], a["R"], NULL) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), EUNSUP),
+    (dict(vb=NULL), EINVAL),
+    (dict(vd=100), EUNSUP),
+    (dict(R=520), EUNSUP),
+    (dict(H=0), EINVAL),
+])
+def test_mla_up_proj_validation(L, kw, code):
+    a = dict(dtype=1, o=P, vb=P, out=P, batch=4, H=16, R=512, vd=128)
+    a.update(kw)
+    assert L.mla_up_proj(a["dtype"], a["o"], a["vb"], a["out"], a["batch"], a["H"], a["R"],
+                         a["vd"], NULL) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=NULL), EINVAL),
+    (dict(bs=24), EINVAL),
+    (dict(maxb=100), EINVAL),              # 100 x 16 < max_seq_len 4096
+    (dict(nb=(1 << 27)), EINVAL),
+])
+def test_mla_paged_validation(L, kw, code):
+    a = dict(dtype=1, q=P, lat=P, o=P, batch=32, H=128, R=512, Pr=64, bt=P, maxb=256, bs=16,
+             nb=9000, lens=P, maxlen=4096, scale=0.072, ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert L.mla_decode_latent_paged(a["dtype"], a["q"], a["lat"], a["o"], a["batch"], a["H"],
+                                     a["R"], a["Pr"], a["bt"], a["maxb"], a["bs"], a["nb"],
+                                     a["lens"], a["maxlen"], a["scale"], a["ws"], a["wsb"],
+                                     NULL) == code
