@@ -2,23 +2,32 @@
 """Throughput of the causal GQA / paged-KV / MLA attention path on one MI355X.
 
 One step is one pass of the whole hot path over seeded synthetic inputs that
-are already resident in HBM:
-  1. paged GQA decode, bf16: 64 sequences, lengths uniform on [512, 8192],
+are already resident in HBM, push then attend:
+  1. push (kv_append) of this step's K/V row of the 64 decode sequences into
+     their paged pool, at position seq_len - 1 (the same row every step);
+  2. paged GQA decode, bf16: 64 sequences, lengths uniform on [512, 8192],
      H=32, Hkv=8, D=128, block size 16, shuffled block tables over a pool
      with 10% slack (attn_decode_paged: split-K partial + combine);
-  2. MLA absorbed latent decode, bf16: 32 sequences x 4096 tokens, 128 heads,
-     latent 512 + 64 (mla_decode_latent);
-  3. chunked prefill on paged K/V, bf16: 8 sequences, 3584 cached + 512 new,
+  3. the same decode with a layer's arms (attn_decode_paged_ext: window 4096,
+     logit softcap 30, ALiBi slopes, sink logits);
+  4. MLA step, bf16, 32 sequences x 4096 tokens, 128 heads, latent 512 + 64:
+     absorb (mla_absorb_q), push of the latent row with k_rot rotated
+     (mla_append_latent), latent attention (mla_decode_latent), value
+     up-projection (mla_up_proj); then the latent attention over a paged
+     copy of the latent (mla_decode_latent_paged, block size 16);
+  5. chunked prefill on paged K/V, bf16: 8 sequences, 3584 cached + 512 new,
      H=32, Hkv=8, scale 0.05 (attn_prefill, paged);
-  4. causal prefill, bf16: B=1, H=28, Hkv=4, D=128, 4096 tokens (attn_prefill).
-The order lets the 1.16 GB decode stream evict the 256 MB Infinity Cache
-before the two workloads whose data would otherwise fit in it.
+  6. ragged chunked prefill on one paged pool, bf16: 16 sequences with chunks
+     U[1, 1024] after U[0, 4096] cached tokens (attn_prefill_varlen);
+  7. causal prefill, bf16: B=1, H=28, Hkv=4, D=128, 4096 tokens (attn_prefill).
+The order lets the 1.16 GB decode streams evict the 256 MB Infinity Cache
+before the workloads whose data would otherwise fit in it.
 
 The headline value is the paged decode's algorithmic HBM bandwidth (each K/V
 byte once, plus Q, O and the block-table entries read) over the duration of
 its call, timed with HIP events on the launch stream; the causal prefill's
-TFLOP/s (causal pairs only) is reported next to it, as are the rooflines of
-every kernel. The CPU baseline times the f64 oracle on a bounded sample.
+TFLOP/s (causal pairs only) is reported next to it, as is the roofline of
+every call. The CPU baseline times the f64 oracle on a bounded sample.
 Prints one JSON line.
 """
 import argparse
@@ -39,7 +48,11 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip", "common.hpp"],
     "prefill": ["prefill.hip", "common.hpp"],
     "mla": ["mla.hip", "common.hpp"],
+    "append": ["append.hip", "common.hpp"],
+    "mla_proj": ["mla_proj.hip", "common.hpp"],
 }
+WORKLOADS = ["append", "decode", "decode_arms", "mla_absorb", "mla_append", "mla", "mla_up",
+             "mla_paged", "chunked", "varlen", "prefill"]
 
 
 def source_digest(kind):
@@ -74,10 +87,11 @@ def parse():
                     help="skip timing the f64 oracle on the host")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle sample")
-    ap.add_argument("--only", choices=["decode", "mla", "chunked", "prefill", "copy"], default=None,
-                    help="time one workload only (for profiler runs); 'copy' runs a plain 1 GiB "
-                         "device copy three times, the calibration for the FETCH_SIZE / "
-                         "WRITE_SIZE counters")
+    ap.add_argument("--only", choices=WORKLOADS + ["copy"], default=None,
+                    help="time one workload only (for profiler runs; the decode arms and the "
+                         "push share the decode inputs, the MLA pieces the MLA inputs); 'copy' "
+                         "runs a plain 1 GiB device copy three times, the calibration for the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -112,14 +126,22 @@ def main():
     def to(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
 
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
     def i32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
-    want = (lambda k: args.only is None or args.only == k)
+    want = (lambda *ks: args.only is None or args.only in ks)
     work = {}
 
-    # ---- 1. paged decode
-    if want("decode"):
+    def add(name, fn, nbytes, flops, bound, kind, kernel):
+        work[name] = dict(fn=fn, bytes=int(nbytes), flops=int(flops), bound=bound, kind=kind,
+                          kernel=kernel)
+
+    # ---- 1-3. push, paged decode, decode with arms
+    d_case = None
+    if want("append", "decode", "decode_arms"):
         d = inputs.paged_decode_case(args.seed)
         dq, dk, dv = to(d.q), to(d.k_pool), to(d.v_pool)
         dbt, dl = i32(d.block_table), i32(d.seq_lens)
@@ -129,56 +151,128 @@ def main():
         dout = torch.empty_like(dq)
         total = int(d.seq_lens.sum())
         blocks = int(((d.seq_lens + 15) // 16).sum())
-        d_bytes = total * 8 * 128 * 2 * 2 + 2 * dq.numel() * 2 + blocks * 4 + 64 * 4
-        work["decode"] = dict(
-            fn=lambda: pk.attn_decode_paged(dq, dk, dv, dbt, dl, max_seq_len=dmax,
-                                            attention_scale=d.scale, out=dout, workspace=dws),
-            bytes=d_bytes, flops=4 * 32 * 128 * total, bound="hbm", kind="decode",
-            kernel="decode_partial + decode_combine")
-        d_case = d
+        kv_bytes = total * 8 * 128 * 2 * 2
+        q_o = 2 * dq.numel() * 2
+        if want("append"):
+            rng = np.random.default_rng(args.seed + 100)
+            kn = to(inputs.to_storage(rng.standard_normal((64, 1, 8, 128), dtype=np.float32), "bf16"))
+            vn = to(inputs.to_storage(rng.standard_normal((64, 1, 8, 128), dtype=np.float32), "bf16"))
+            pos = i32(d.seq_lens - 1)      # this step's row: the last of each sequence
+            add("append", lambda: pk.kv_append(kn, vn, dk, dv, pos, block_table=dbt),
+                64 * 8 * 128 * 2 * 2 * 2 + 64 * 4 * 2, 0, "hbm", "append", "kv_append_kernel")
+        if want("decode"):
+            add("decode", lambda: pk.attn_decode_paged(dq, dk, dv, dbt, dl, max_seq_len=dmax,
+                                                       attention_scale=d.scale, out=dout,
+                                                       workspace=dws),
+                kv_bytes + q_o + blocks * 4 + 64 * 4, 4 * 32 * 128 * total, "hbm", "decode",
+                "decode_partial + decode_combine")
+            d_case = d
+        if want("decode_arms"):
+            slopes, sinks = f32(inputs.alibi_slopes(32)), f32(inputs.sink_logits(args.seed, 32))
+            eff = np.minimum(d.seq_lens, 4096)
+            e_tot = int(eff.sum())
+            add("decode_arms",
+                lambda: pk.attn_decode_paged_ext(dq, dk, dv, dbt, dl, max_seq_len=dmax,
+                                                 attention_scale=d.scale, window=4096,
+                                                 softcap=30.0, alibi=slopes, sinks=sinks,
+                                                 out=dout, workspace=dws),
+                e_tot * 8 * 128 * 2 * 2 + q_o + int(((eff + 15) // 16).sum()) * 4 + 64 * 4 +
+                2 * 32 * 4, 4 * 32 * 128 * e_tot, "hbm", "decode",
+                "decode_partial<ext> + decode_combine<ext>")
 
-    # ---- 2. MLA latent decode
-    if want("mla"):
+    # ---- 4. MLA step
+    if want("mla_absorb", "mla_append", "mla", "mla_up", "mla_paged"):
         m = inputs.mla_case(args.seed)
         mq, ml, mlens = to(m.q_abs), to(m.latent), i32(m.seq_lens)
         mout = torch.empty((32, 128, 512), dtype=torch.bfloat16, device=dev)
         mws = torch.empty(max(16, pk.mla_decode_workspace_size(32, 128, 512, 4096)),
                           dtype=torch.uint8, device=dev)
-        work["mla"] = dict(
-            fn=lambda: pk.mla_decode_latent(mq, ml, mlens, kv_lora_rank=512, max_seq_len=4096,
-                                            attention_scale=m.scale, out=mout, workspace=mws),
-            bytes=ml.numel() * 2 + mq.numel() * 2 + mout.numel() * 2 + 32 * 4,
-            flops=32 * 128 * 4096 * (2 * 576 + 2 * 512), bound="hbm", kind="mla",
-            kernel="mla_kernel + mla_combine")
+        lat_bytes = 32 * 4096 * 576 * 2
+        if want("mla_absorb", "mla_up"):
+            w = inputs.mla_proj_case(args.seed)
+            wq, wkb, wvb = to(w.q), to(w.k_b), to(w.v_b)
+            wup = torch.empty((32, 128, 128), dtype=torch.bfloat16, device=dev)
+            proj_flops = 2 * 32 * 128 * 512 * 128
+            if want("mla_absorb"):
+                add("mla_absorb", lambda: pk.mla_absorb_q(wq, wkb, out=mq),
+                    wkb.numel() * 2 + wq.numel() * 2 + mq.numel() * 2, proj_flops, "hbm",
+                    "mla_proj", "mla_proj_kernel (absorb)")
+        if want("mla_append"):
+            a = inputs.mla_append_case(args.seed + 1, batch=1, held=[0])
+            cn = to(np.repeat(a.c_new, 32, axis=0))
+            kr = to(np.repeat(a.k_rot_new, 32, axis=0))
+            mpos = i32(m.seq_lens - 1)
+            add("mla_append", lambda: pk.mla_append_latent(cn, kr, ml, mpos, rope_theta=1e4),
+                32 * 576 * 2 * 2 + 32 * 4, 0, "hbm", "append", "mla_append_kernel")
+        if want("mla"):
+            add("mla", lambda: pk.mla_decode_latent(mq, ml, mlens, kv_lora_rank=512,
+                                                    max_seq_len=4096, attention_scale=m.scale,
+                                                    out=mout, workspace=mws),
+                lat_bytes + mq.numel() * 2 + mout.numel() * 2 + 32 * 4,
+                32 * 128 * 4096 * (2 * 576 + 2 * 512), "hbm", "mla", "mla_kernel + mla_combine")
+        if want("mla_up"):
+            add("mla_up", lambda: pk.mla_up_proj(mout, wvb, out=wup),
+                wvb.numel() * 2 + mout.numel() * 2 + wup.numel() * 2, proj_flops, "hbm",
+                "mla_proj", "mla_proj_kernel (up-projection)")
+        if want("mla_paged"):
+            rng = np.random.default_rng(args.seed + 7)
+            nblk = 32 * 4096 // 16
+            perm = rng.permutation(nblk + nblk // 10)
+            mbt = perm[:nblk].reshape(32, 256).astype(np.int32)
+            pool = torch.empty((nblk + nblk // 10, 16, 576), dtype=torch.bfloat16, device=dev)
+            pool[torch.from_numpy(mbt.reshape(-1)).long().to(dev)] = ml.reshape(nblk, 16, 576)
+            mbt_d = i32(mbt)
+            mpout = torch.empty_like(mout)
+            add("mla_paged", lambda: pk.mla_decode_latent_paged(mq, pool, mbt_d, mlens,
+                                                                kv_lora_rank=512, max_seq_len=4096,
+                                                                attention_scale=m.scale, out=mpout,
+                                                                workspace=mws),
+                lat_bytes + mq.numel() * 2 + mout.numel() * 2 + 32 * 4 + nblk * 4,
+                32 * 128 * 4096 * (2 * 576 + 2 * 512), "hbm", "mla",
+                "mla_kernel<paged> + mla_combine")
         m.latent = m.q_abs = None
 
-    # ---- 3. chunked prefill on paged K/V
+    # ---- 5. chunked prefill on paged K/V
     if want("chunked"):
         c = inputs.chunked_paged_prefill_case(args.seed)
         cq, ck, cv, cbt = to(c.q), to(c.k), to(c.v), i32(c.block_table)
         cout = torch.empty_like(cq)
         pairs = sum(c.position_offset + i + 1 for i in range(c.seq_q)) * c.batch
-        work["chunked"] = dict(
-            fn=lambda: pk.attn_prefill(cq, ck, cv, seq_kv=c.seq_kv, position_offset=c.position_offset,
-                                       attention_scale=c.scale, block_table=cbt, out=cout),
-            bytes=(c.batch * c.seq_kv * 8 * 128 * 2 * 2) + 2 * cq.numel() * 2,
-            flops=4 * 128 * 32 * pairs, bound="mfma", kind="prefill", kernel="prefill_kernel")
+        add("chunked", lambda: pk.attn_prefill(cq, ck, cv, seq_kv=c.seq_kv,
+                                               position_offset=c.position_offset,
+                                               attention_scale=c.scale, block_table=cbt, out=cout),
+            (c.batch * c.seq_kv * 8 * 128 * 2 * 2) + 2 * cq.numel() * 2, 4 * 128 * 32 * pairs,
+            "mfma", "prefill", "prefill_kernel")
         c.q = c.k = c.v = None
 
-    # ---- 4. causal prefill
+    # ---- 6. ragged chunked prefill
+    if want("varlen"):
+        r = inputs.varlen_prefill_case(args.seed)
+        rq, rk, rv, rbt = to(r.q), to(r.k), to(r.v), i32(r.block_table)
+        rcu, rkv = i32(r.cu_q), i32(r.seq_kv)
+        rout = torch.empty_like(rq)
+        rmax = int(r.q_lens.max())
+        pairs = sum(int(r.seq_kv[b] - r.q_lens[b]) * int(r.q_lens[b]) +
+                    int(r.q_lens[b]) * (int(r.q_lens[b]) + 1) // 2 for b in range(r.batch))
+        add("varlen", lambda: pk.attn_prefill_varlen(rq, rk, rv, rcu, rkv, max_seq_q=rmax,
+                                                     attention_scale=r.scale, block_table=rbt,
+                                                     out=rout),
+            int(r.seq_kv.sum()) * 8 * 128 * 2 * 2 + 2 * rq.numel() * 2, 4 * 128 * 32 * pairs,
+            "mfma", "prefill", "prefill_kernel<varlen>")
+        r.q = r.k = r.v = None
+
+    # ---- 7. causal prefill
     if want("prefill"):
         p = inputs.prefill_case(args.seed)
         pq, pk_, pv = to(p.q), to(p.k), to(p.v)
         pout = torch.empty_like(pq)
-        work["prefill"] = dict(
-            fn=lambda: pk.attn_prefill(pq, pk_, pv, seq_kv=p.seq_kv, position_offset=0,
-                                       attention_scale=p.scale, out=pout),
-            bytes=pq.numel() * 2 * 2 + pk_.numel() * 2 * 2,
-            flops=4 * 128 * 28 * (4096 * 4097 // 2), bound="mfma", kind="prefill",
-            kernel="prefill_kernel")
+        add("prefill", lambda: pk.attn_prefill(pq, pk_, pv, seq_kv=p.seq_kv, position_offset=0,
+                                               attention_scale=p.scale, out=pout),
+            pq.numel() * 2 * 2 + pk_.numel() * 2 * 2, 4 * 128 * 28 * (4096 * 4097 // 2), "mfma",
+            "prefill", "prefill_kernel")
         p.q = p.k = p.v = None
 
-    order = [k for k in ("decode", "mla", "chunked", "prefill") if k in work]
+    order = [k for k in WORKLOADS if k in work]
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
@@ -208,7 +302,8 @@ def main():
         ts = np.array([evs[s][k][0].elapsed_time(evs[s][k][1]) for s in range(args.steps)]) * 1e-3
         w = work[k]
         avg = float(ts.mean())
-        res[k] = dict(us_avg=avg * 1e6, us_min=float(ts.min()) * 1e6, us_median=float(np.median(ts)) * 1e6,
+        res[k] = dict(us_avg=avg * 1e6, us_min=float(ts.min()) * 1e6,
+                      us_median=float(np.median(ts)) * 1e6,
                       gbps=w["bytes"] / avg / 1e9, tflops=w["flops"] / avg / 1e12)
 
     def roofline(k):
@@ -226,9 +321,12 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "paged GQA decode bf16 (64 seqs, seq_lens U[512,8192], H=32 Hkv=8 "
-                                   "D=128, block 16) + MLA latent decode bf16 (32x4096, H=128, 512+64) "
-                                   "+ chunked paged prefill bf16 (8 x (3584+512), H=32 Hkv=8) + causal "
-                                   "prefill bf16 (B=1 S=4096 H=28 Hkv=4 D=128)",
+                                   "D=128, block 16) with its K/V push and an arms variant + MLA "
+                                   "step bf16 (32x4096, H=128, 512+64: absorb, latent push, latent "
+                                   "decode contiguous and paged, up-projection) + chunked paged "
+                                   "prefill bf16 (8 x (3584+512), H=32 Hkv=8) + ragged paged "
+                                   "prefill bf16 (16 seqs) + causal prefill bf16 (B=1 S=4096 H=28 "
+                                   "Hkv=4 D=128)",
                        "seed": args.seed, "parallelism": "single GPU"}}
     if "decode" in res:
         line["value"] = round(res["decode"]["gbps"], 2)
@@ -245,7 +343,7 @@ def main():
     line["kernels"] = {k: {kk: round(vv, 3) for kk, vv in res[k].items()} for k in order}
 
     # ---- CPU baseline: the f64 oracle on a bounded sample of the paged decode
-    if not args.no_cpu_baseline and "decode" in work:
+    if not args.no_cpu_baseline and d_case is not None:
         line["cpu_baseline"] = cpu_baseline(d_case, args.cpu_seconds, args.seed)
     print(json.dumps(line), flush=True)
 
