@@ -24,6 +24,12 @@ __device__ __forceinline__ void store_nt(V* p, V v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// Non-temporal 16-byte load for data read exactly once (streamed K/V rows).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ------------------------------------------------ global -> LDS copies
 // s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in [15:14]; the others at their maximum).

@@ -44,6 +44,12 @@ constexpr int kUnroll = PKVA_DECODE_UNROLL;  // tokens per batch per lane group 
 #define PKVA_DECODE_WAVES_G4 3
 #endif
 constexpr int kWavesG4 = PKVA_DECODE_WAVES_G4;  // waves per SIMD the group-of-4 kernels are built for
+#ifndef PKVA_DECODE_SLOTS_PCT
+#define PKVA_DECODE_SLOTS_PCT 100
+#endif
+// Ranges per launch, in percent of the resident workgroup slots: above 100
+// the dispatcher hands the later ranges to whichever unit frees a slot first.
+constexpr int kSlotsPct = PKVA_DECODE_SLOTS_PCT;
 constexpr int kBtWin = 1024;     // block-table entries cached in LDS per sub-piece
 constexpr float kLazy = 8.0f;    // log2 headroom before the running max is moved
 constexpr float kLog2e = 1.4426950408889634f;
@@ -284,12 +290,15 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
         return PAGED ? (uint32_t)((s_blk[(t >> shift) - blk0] << shift) + (t & bs_mask))
                      : (uint32_t)(seq_row0 + t);
       };
+      // K and V bytes are read exactly once: non-temporal loads keep them from
+      // displacing other lines in the caches (and from the write-back of dirty
+      // lines they would otherwise force).
       auto load_rows = [&](uint4 (&x)[U], const char* base, uint32_t row_bytes, int t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int t = t0 + u * R;
           x[u] = make_uint4(0, 0, 0, 0);
-          if (t < c1) x[u] = *(const uint4*)(base + row_of(t) * row_bytes);
+          if (t < c1) x[u] = load_nt16(base + row_of(t) * row_bytes);
         }
       };
       // K rows: the lane's chunk, and its second chunk when the keys are wider.
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4
           for (int u = 0; u < U; ++u) {
             const int t = t0 + u * R;
             xx[u] = make_uint4(0, 0, 0, 0);
-            if (li < LX && t < c1) xx[u] = *(const uint4*)(kxbase0 + row_of(t) * k_row_bytes);
+            if (li < LX && t < c1) xx[u] = load_nt16(kxbase0 + row_of(t) * k_row_bytes);
           }
         }
       };
@@ -570,7 +579,7 @@ int resident_ranges(const DecodeParams& p) {
     g_cus[dev].store(cus, std::memory_order_relaxed);
     slots_per_cu[dev].store(occ, std::memory_order_relaxed);
   }
-  const int slots = cus * occ / p.nslab;
+  const int slots = (int)((int64_t)cus * occ * kSlotsPct / 100 / p.nslab);
   return max(1, min(p.n_ranges, slots));
 }
 
