@@ -382,17 +382,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   };
 
   if (n_t > 0) {
-    // Prologue: tiles 0 .. kPrefetch-1 in flight, Q^T loaded meanwhile, then
-    // every load done (no load the compiler tracks is pending in the loop),
-    // tile 0 published, its scores.
-    for (int i = 0; i < kPrefetch && i < n_t; ++i) issue(i);
+    // Prologue: tile 0 and Q^T, then every load done (no load the compiler
+    // tracks is pending from here on); tiles 1 .. kPrefetch-1 go out only now,
+    // so that the first scores wait for one tile instead of three; tile 0
+    // published (its copies landed before the later ones were issued), its
+    // scores.
+    issue(0);
     {
       const __bf16* qg = (const __bf16*)p.q + ((int64_t)b * p.n_heads + head) * kW + 8 * hf;
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) qB[kk] = *(const bf16x8_t*)(qg + 16 * kk);
     }
     wait_vmcnt<0>();
-    publish(0);
+    for (int i = 1; i < kPrefetch && i < n_t; ++i) issue(i);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     // One score tile is enough: the softmax turns it into P (pb) before the
     // next tile's scores are computed into the same registers.
     f32x16_t sc;
@@ -463,36 +468,57 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   }
 }
 
-// Merge the splits of each (sequence, head) in split order: 128 threads per
-// head, four values per thread. Split s contributes 2^(m_s - M) * l_s times
-// its normalised partial.
+// Merge the splits of each (sequence, head) in split order: one wave per
+// head, eight values per lane. Split s contributes 2^(m_s - M) l_s times its
+// normalised partial, with a running maximum M; the loads of up to
+// kCombineBatch splits are issued together, so a sequence costs one memory
+// round trip per batch.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineHeads = kCombineThreads / (kR / 4);   // heads per workgroup
+constexpr int kCombineHeads = kCombineThreads / (kR / 8);   // heads per workgroup
+constexpr int kCombineBatch = 8;
 __global__ __launch_bounds__(kCombineThreads) void mla_combine(MlaParams p) {
-  const int hh = threadIdx.x / (kR / 4);
-  const int d = 4 * (threadIdx.x % (kR / 4));
+  const int hh = threadIdx.x / (kR / 8);
+  const int d = 8 * (threadIdx.x % (kR / 8));
   const int bh = blockIdx.x * kCombineHeads + hh;   // b * n_heads + h
   const int b = bh / p.n_heads, h = bh % p.n_heads;
   const int L = p.seq_lens[b];
   const bool bad = L < 1 || L > p.max_seq_len;
   const int nsp = bad ? 0 : (L + p.split_tokens - 1) / p.split_tokens;
   const int64_t w0 = (int64_t)b * p.nsplit * p.n_heads + h;   // split s: w0 + s * n_heads
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, p.ws_ml[(w0 + (int64_t)s * p.n_heads) * 2]);
-  f32x4_t num = f32x4_t{};
-  float den = 0.0f;
-  for (int s = 0; s < nsp; ++s) {
-    const int64_t w = w0 + (int64_t)s * p.n_heads;
-    const float wl = __builtin_amdgcn_exp2f(p.ws_ml[w * 2] - M) * p.ws_ml[w * 2 + 1];
-    den += wl;
-    const bf16x4_t o = *(const bf16x4_t*)(p.ws_o + w * kR + d);
+  float M = -INFINITY, den = 0.0f;
+  float num[8] = {};
+  for (int s0 = 0; s0 < nsp; s0 += kCombineBatch) {
+    float mm[kCombineBatch], ll[kCombineBatch];
+    bf16x8_t oo[kCombineBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) num[j] = fmaf(wl, (float)o[j], num[j]);
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const bool ok = s0 + j < nsp;
+      const int64_t w = w0 + (int64_t)(s0 + j) * p.n_heads;
+      mm[j] = ok ? p.ws_ml[w * 2] : -INFINITY;
+      ll[j] = ok ? p.ws_ml[w * 2 + 1] : 0.0f;
+      oo[j] = ok ? *(const bf16x8_t*)(p.ws_o + w * kR + d) : bf16x8_t{};
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (s0 + j < nsp) {
+        const float Mn = fmaxf(M, mm[j]);
+        const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+        // Every split below nsp holds tokens, so its m is finite, unless a
+        // block outside the pool poisoned it (m = -inf, l = NaN): then wl is
+        // NaN and so is the row.
+        const float wl = __builtin_amdgcn_exp2f(mm[j] - Mn) * ll[j];
+        den = fmaf(den, a, wl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] = fmaf(wl, (float)oo[j][e], num[e] * a);
+        M = Mn;
+      }
+    }
   }
   const float inv = bad ? __builtin_nanf("") : 1.0f / den;
-  const bf16x4_t out = {(__bf16)(num[0] * inv), (__bf16)(num[1] * inv), (__bf16)(num[2] * inv),
-                        (__bf16)(num[3] * inv)};
-  store_nt((bf16x4_t*)((__bf16*)p.o + (int64_t)bh * kR + d), out);
+  bf16x8_t out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (__bf16)(num[e] * inv);
+  store_nt((bf16x8_t*)((__bf16*)p.o + (int64_t)bh * kR + d), out);
 }
 
 template <int NW>
