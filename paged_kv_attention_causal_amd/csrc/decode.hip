@@ -126,11 +126,19 @@ __device__ __forceinline__ int span_len(const DecodeParams& p, int b, int* start
   return L;
 }
 
+// tanh(y) = 1 - 2 / (1 + e^(2y)): exp2 and a reciprocal; it saturates to
+// +-1 for large |y| (e^(2y) -> inf or 0) and loses only absolute precision
+// (about 1e-7) near 0.
+__device__ __forceinline__ float tanh_fast(float y) {
+  const float e = __builtin_amdgcn_exp2f(y * (2.0f * kLog2e));
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // The logit of a score in the exp2 domain with the layer's arms:
 // x = scale * s, then softcap * tanh(x / softcap), plus slope * (t - pos).
 __device__ __forceinline__ float arm_logit(const DecodeParams& p, float s, float slope, int rel) {
   float x = s * p.scale;
-  if (p.softcap > 0.0f) x = p.softcap * tanhf(x * p.inv_softcap);
+  if (p.softcap > 0.0f) x = p.softcap * tanh_fast(x * p.inv_softcap);
   x = fmaf(slope, (float)rel, x);
   return x * kLog2e;
 }
