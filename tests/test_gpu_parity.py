@@ -128,6 +128,10 @@ PREFILL_CASES = [
     (1, 4, 2, 16, 77, 5, 0, 0, "f32", 0.25),
     (2, 6, 3, 16, 130, 0, 0, 4, "f32", 0.7),
     (1, 2, 1, 128, 40, 0, 0, 0, "bf16", 0.0),         # scale 0: uniform weights
+    # chunks no longer than their history: items grouped by KV head, with a
+    # whole XCD run plus a tail, and an all-tail grid
+    (5, 6, 3, 128, 300, 400, 0, 16, "bf16", None),
+    (3, 8, 2, 128, 513, 600, 0, 0, "bf16", None),
 ]
 
 
