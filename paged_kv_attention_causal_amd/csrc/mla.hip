@@ -87,7 +87,18 @@ __device__ __forceinline__ bf16x4_t ds_read_tr16(const char* p) {
   return __builtin_bit_cast(bf16x4_t, v);
 }
 
-__device__ __forceinline__ int swz(int r) { return 2 * (r % 4) + (r / 4) % 2; }
+// Tile image in LDS: nine 4 KB column blocks; block c8 holds chunks
+// 8 c8 .. 8 c8 + 7 (128 bytes) of all 32 rows, and chunk c of row r sits at
+// 4096 (c / 8) + 128 r + 16 ((c % 8) ^ swz(r)). Rows r and r + 2 start on the
+// same banks (of the 64 4-byte banks, 256 bytes, the LDS serves per clock):
+// the eight rows of one parity among 16 consecutive ones take the eight XOR
+// values, so a K-fragment read (16 lanes = 16 rows, one chunk) hits 16
+// distinct 16-byte bank groups, and rows 4k and 4k + 2 differ in bit 2,
+// which keeps the four-chunk groups of a V^T read apart.
+__device__ __forceinline__ int swz(int r) {
+  const int m = (r >> 1) & 7;
+  return 4 * (m & 1) + (m >> 1);
+}
 
 // acc *= alpha with acc kept in accumulation registers (read, scale and write
 // back in place; plain VALU arithmetic on them makes the compiler move all of
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   const int shift = p.block_shift;
   const int32_t* bt_row = PAGED ? p.block_table + (int64_t)b * p.max_blocks_per_seq : nullptr;
   int win0 = 0, win_end = 0;   // block ids [win0, win_end) of the sequence held in s_bt
-  auto load_window = [&](int blk) {
+  auto load_window = [&](int blk) __attribute__((always_inline)) {
     __syncthreads();   // no wave still reads the old window
     win0 = blk;
     win_end = min(blk + kBtWin, ((t_end - 1) >> shift) + 1);
@@ -176,52 +187,62 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   }
   const int n_t = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
-  // Copy tile i (tokens t_begin + 32 i ..) into its stage. DMA op j of this
-  // wave covers bytes [1024 ins, +1024) of the tile, ins = wave + NW * j,
-  // i.e. chunk slots 64 ins + lane in row-major order; the lane brings the
-  // chunk the swizzle puts there, at byte dma_off[j] of the tile's rows in
-  // global memory. Rows past t_end copy row t_end - 1 instead (their scores
-  // are masked; a NaN beyond the context must not reach P * V), so every
-  // thread issues the same number of copies per tile and the counted waits
-  // hold.
-  uint32_t dma_off[kDmaPerThread];
+  // Copy tile i (tokens t_begin + 32 i ..) into its stage. DMA op J of a
+  // tile (1 KB, LDS bytes [1024 J, +1024)) covers column block J / 4, rows
+  // 8 u .. 8 u + 7 with u = J % 4: lane l brings row 8 u + l / 8, chunk
+  // 8 (J / 4) + ((l % 8) ^ swz(row)), which lies at byte
+  // dlane[u % 2] + 8 u kRowB + 128 (J / 4) of the tile's rows (swz has period
+  // 16, so the lane part depends on u % 2 only). This wave issues ops
+  // J = wave + NW j. Rows past t_end copy row t_end - 1 instead (their
+  // scores are masked; a NaN beyond the context must not reach P * V), so
+  // every thread issues the same number of copies per tile and the counted
+  // waits hold.
+  const int drow = lane / 8;
+  uint32_t dlane[2];
 #pragma unroll
-  for (int j = 0; j < kDmaPerThread; ++j) {
-    const int q = 64 * (wave + NW * j) + lane;
-    const int row = q / kChunks, slot = q % kChunks;
-    dma_off[j] = (uint32_t)(row * kRowB + 16 * (slot ^ swz(row)));
-  }
-  auto issue = [&](int i) {
-    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(s_lat) +
-                        (uint32_t)((i % kStages) * kTileB);
-    const int t0 = t_begin + kTile * i;
+  for (int u2 = 0; u2 < 2; ++u2)
+    dlane[u2] = (uint32_t)(drow * kRowB + 16 * ((lane % 8) ^ swz(8 * u2 + drow)));
+  // issue_prep(i) runs on every wave at the same point (a paged window reload
+  // takes barriers); issue_op(i, j) then issues DMA op j of tile i, so the
+  // ops of a tile can be spread between the MFMAs of a step.
+  auto issue_prep = [&](int i) __attribute__((always_inline)) {
     if constexpr (PAGED) {
+      const int t0 = t_begin + kTile * i;
       const int last = min(t_end - 1 - t0, kTile - 1);   // last live row of the tile
       if (((t0 + last) >> shift) >= win_end) load_window(t0 >> shift);   // uniform
+    }
+  };
+  // MODE 1: a whole contiguous tile (one lane offset, the rest uniform);
+  // MODE 2: the last, partial tile of a contiguous range, or a paged tile.
+  auto issue_op = [&](int i, int j, auto mode) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
+    const int J = wave + NW * j, u = J % 4, c8 = J / 4;
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(s_lat) +
+                        (uint32_t)((i % kStages) * kTileB) + 1024u * J;
+    const int t0 = t_begin + kTile * i;
+    if constexpr (PAGED) {
+      const int last = min(t_end - 1 - t0, kTile - 1);
       const int bs_mask = (1 << shift) - 1;
-#pragma unroll
-      for (int j = 0; j < kDmaPerThread; ++j) {
-        const int row = (int)(dma_off[j] / kRowB);
-        const uint32_t chunk = dma_off[j] - (uint32_t)(row * kRowB);
-        const int t = t0 + min(row, last);
-        const uint32_t prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
-        dma16_addr(lat + (uint64_t)prow * kRowB + chunk, st + 1024u * (wave + NW * j));
-      }
+      const int t = t0 + min(8 * u + drow, last);
+      const uint32_t prow = (uint32_t)((s_bt[(t >> shift) - win0] << shift) + (t & bs_mask));
+      dma16_addr(lat + (uint64_t)prow * kRowB + (dlane[u & 1] - drow * kRowB) + 128 * c8, st);
       return;
     }
-    const char* base = lat + (int64_t)t0 * kRowB;
-    if (t0 + kTile <= t_end) {
-#pragma unroll
-      for (int j = 0; j < kDmaPerThread; ++j) dma16(base, dma_off[j], st + 1024u * (wave + NW * j));
+    if constexpr (MODE == 1) {
+      dma16(lat + (int64_t)(t0 + 8 * u) * kRowB + 128 * c8, dlane[u & 1], st);
     } else {
-      const int last = t_end - 1 - t0;   // last live row of the tile
-#pragma unroll
-      for (int j = 0; j < kDmaPerThread; ++j) {
-        const int row = (int)(dma_off[j] / kRowB);
-        const uint32_t off = dma_off[j] - (uint32_t)((row - min(row, last)) * kRowB);
-        dma16(base, off, st + 1024u * (wave + NW * j));
-      }
+      // The lane's row is clamped to the last live one; the offset (which
+      // the instruction takes as unsigned) stays relative to the tile start.
+      const int last = min(t_end - 1 - t0, kTile - 1);   // last live row of the tile
+      const int row = 8 * u + drow;
+      dma16(lat + (int64_t)t0 * kRowB + 128 * c8,
+            dlane[u & 1] + (uint32_t)((8 * u - (row - min(row, last))) * kRowB), st);
     }
+  };
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    issue_prep(i);
+#pragma unroll
+    for (int j = 0; j < kDmaPerThread; ++j) issue_op(i, j, std::integral_constant<int, 2>{});
   };
   // publish(i) runs when the tiles up to min(i + kPrefetch - 2, n_t - 1) are
   // issued: wait until at most the later tiles' copies are in flight (vmcnt
@@ -230,7 +251,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // a wave reads tile j's stage in steps j - 1 (its keys) and j (its
   // values), and the copy of tile j + 4 into that stage is issued only after
   // publish(j + 2), which no wave passes before it has finished step j.
-  auto publish = [&](int i) {
+  auto publish = [&](int i) __attribute__((always_inline)) {
     const int later = max(0, min(i + kPrefetch - 2, n_t - 1) - i);
     static_assert(kPrefetch - 2 <= 1, "extend the wait cases");
     // (vmcnt holds at most 63: waiting for fewer in flight is also correct.)
@@ -247,28 +268,24 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   };
 
   // Per-lane LDS offsets inside a tile (the rest is an immediate):
-  //   K fragment of S^T (A operand): row lr, chunk 2*kk + hf swizzled by
-  //   swz(lr), which flips kk bits 0-1: one base per kk % 4;
-  //   V^T fragment: lane (g16, i16) reads row 16*mm + 4*hf + i16/4 (+8 for
-  //   the upper half), chunk 4*db + 2*(g16%2) + (i16%4)/2, half i16 % 2; the
-  //   swizzle flips db parity for half the lanes: one base per db parity.
+  //   K fragment of S^T (A operand): row lr, chunk 2 kk + hf, in column block
+  //   kk / 4: one base per kk % 4;
+  //   V^T fragment: lane (g16, i16) reads row 16 mm + 4 hf + i16 / 4 (+8 for
+  //   the upper half), chunk 4 db + 2 (g16 % 2) + (i16 % 4) / 2, half
+  //   i16 % 2, in column block db / 2: one base per (db parity, half).
   const int g16 = lane / 16, i16 = lane % 16;
   int k_base[4];
-  {
-    const int sk = swz(lr);
-    const int lb = lr * kRowB + 16 * (hf ^ (sk & 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k_base[j] = lb + 32 * ((j ^ (sk >> 1)) - j);
-  }
-  int v_even, v_odd;
-  {
-    const int r = 4 * hf + i16 / 4;
-    const int sv = swz(r);
-    const int cl = 2 * (g16 % 2) + (i16 % 4) / 2;
-    const int lb = r * kRowB + 16 * (cl ^ (sv & 3)) + 8 * (i16 % 2);
-    v_even = lb + 64 * (sv >> 2);
-    v_odd = lb - 64 * (sv >> 2);
-  }
+  for (int j = 0; j < 4; ++j) k_base[j] = 128 * lr + 16 * ((2 * j + hf) ^ swz(lr));
+  int v_base[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * hf + i16 / 4 + 8 * h;
+      const int cl = 2 * (g16 % 2) + (i16 % 4) / 2;
+      v_base[par][h] = 128 * r + 16 * ((4 * par + cl) ^ swz(r)) + 8 * (i16 % 2);
+    }
 
   bf16x8_t qB[kKSteps];   // Q^T as the B operand: head lr, dims 16*kk + 8*hf .. +7
   f32x16_t oacc[kDB];
@@ -284,18 +301,25 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // Operand reads run kAhead MFMA pairs ahead through register rings;
   // the scheduling barriers keep the compiler from hoisting all 68 reads
   // (which would not fit in registers).
-  auto read_k = [&](const char* sk, int kk) {
-    return *(const bf16x8_t*)(sk + k_base[kk % 4] + 32 * kk);
+  auto read_k = [&](const char* sk, int kk) __attribute__((always_inline)) {
+    return *(const bf16x8_t*)(sk + k_base[kk % 4] + 4096 * (kk / 4));
   };
-  auto read_v = [&](const char* sv, int idx) {   // idx = 16 * mm + db
+  auto read_v = [&](const char* sv, int idx) __attribute__((always_inline)) {   // idx = 16 * mm + db
     const int mm = idx / kDB, db = idx % kDB;
-    const char* vb = sv + ((db & 1) ? v_odd : v_even) + 16 * mm * kRowB + 64 * db;
-    const bf16x4_t lo = ds_read_tr16(vb);
-    const bf16x4_t hi = ds_read_tr16(vb + 8 * kRowB);
+    const char* vb = sv + 4096 * (db / 2) + 2048 * mm;
+    const bf16x4_t lo = ds_read_tr16(vb + v_base[db & 1][0]);
+    const bf16x4_t hi = ds_read_tr16(vb + v_base[db & 1][1]);
     return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  auto scores_and_values = [&](f32x16_t& s, int stage, int pv_stage, auto with_pv) {
+  // When dma_tile >= 0, the copies of that tile are issued one every
+  // kDmaStride MFMA steps: an op that has to wait for room in the memory
+  // queues then stalls a wave for part of an MFMA's latency, not all at once.
+  constexpr int kDmaStride = kKSteps / kDmaPerThread;
+  static_assert(kKSteps % kDmaPerThread == 0, "DMA ops spread evenly over the score steps");
+  auto scores_and_values = [&](f32x16_t& s, int stage, int pv_stage, auto with_pv, int dma_tile,
+                               auto dma_mode) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
+    constexpr int DMA = decltype(dma_mode)::value;   // 0: no copies, else issue_op's MODE
     const char* sk = s_lat + stage * kTileB;
     const char* sv = s_lat + pv_stage * kTileB;
     bf16x8_t kr[kAhead + 1], vr[kAhead + 1];
@@ -319,11 +343,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
         const int mm = kk / kDB, db = kk % kDB;
         oacc[db] = mma(vr[kk % (kAhead + 1)], pb[mm], oacc[db]);
       }
+      if (DMA != 0 && kk % kDmaStride == 0) issue_op(dma_tile, kk / kDmaStride, dma_mode);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // O^T += V^T P^T alone (the last tile of the range).
-  auto values = [&](int pv_stage) {
+  auto values = [&](int pv_stage) __attribute__((always_inline)) {
     const char* sv = s_lat + pv_stage * kTileB;
     bf16x8_t vr[kAhead + 1];
 #pragma unroll
@@ -341,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // P in bf16 (pb) and the row sum of the same rounded values. Accumulator
   // register r holds token 32 i + 8*(r/4) + 4*hf + r%4 of the range.
   const uint32_t ones = 0x3f803f80u;
-  auto softmax = [&](f32x16_t& s, int i) {
+  auto softmax = [&](f32x16_t& s, int i) __attribute__((always_inline)) {
     score_wait();
     const int t0 = t_begin + kTile * i;
     if (t0 + kTile > t_end) {
@@ -382,39 +407,97 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   };
 
   if (n_t > 0) {
-    // Prologue: tile 0 and Q^T, then every load done (no load the compiler
-    // tracks is pending from here on); tiles 1 .. kPrefetch-1 go out only now,
-    // so that the first scores wait for one tile instead of three; tile 0
-    // published (its copies landed before the later ones were issued), its
-    // scores.
-    issue(0);
+    // Prologue. Q^T first: each wave copies its 32 heads' rows (36 KB,
+    // contiguous in q_abs) into its own stage of the ring with 1 KB DMA ops
+    // in the tile layout, waits for its own copies and reads Q^T from there
+    // with the K-fragment pattern (lane (lr, hf) gets row lr, chunk
+    // 2 kk + hf: the B operand). Loading it straight into registers would
+    // touch 32 rows with 32 bytes each per instruction. Then tiles 0 .. 2;
+    // tile 0 published, its scores.
+    // While Q^T is in flight, one dword of every 128-byte line of tiles
+    // 0 .. 2 is loaded (and dropped): the lines are then in the caches when
+    // those tiles are copied after the barrier, instead of every workgroup
+    // asking for its first three tiles from memory at the same moment.
+    constexpr int kPfLines = kPrefetch * kTile * (kRowB / 128);
+    constexpr int kPf = (kPfLines + 64 * NW - 1) / (64 * NW);   // loads per thread
+    uint32_t touched = 0;
     {
-      const __bf16* qg = (const __bf16*)p.q + ((int64_t)b * p.n_heads + head) * kW + 8 * hf;
+      const char* qg = (const char*)p.q + ((int64_t)b * p.n_heads + (hg * NW + wave) * kHW) * kRowB;
+      const uint32_t qst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(s_lat) +
+                           (uint32_t)(wave * kTileB);
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qB[kk] = *(const bf16x8_t*)(qg + 16 * kk);
+      for (int J = 0; J < kDmaTile; ++J)
+        dma16(qg + 8 * (J % 4) * kRowB + 128 * (J / 4), dlane[J % 2], qst + 1024u * J);
+      const int rows = min(t_end - t_begin, kPrefetch * kTile);
+#pragma unroll
+      for (int k = 0; k < kPf; ++k) {
+        const int l = min(tid + 64 * NW * k, kPfLines - 1);
+        const int t = t_begin + min(l / (kRowB / 128), rows - 1);
+        const int col = l % (kRowB / 128);
+        int64_t row;
+        if constexpr (PAGED) {
+          row = ((int64_t)s_bt[(t >> shift) - win0] << shift) + (t & ((1 << shift) - 1));
+        } else {
+          row = t;
+        }
+        touched ^= *(const uint32_t*)(lat + row * kRowB + 128 * col);
+      }
+      // Wait for everything: a counted wait would assume that the copies to
+      // LDS and the loads to registers complete in issue order.
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      const char* sq = s_lat + wave * kTileB;
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) qB[kk] = read_k(sq, kk);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): Q^T is in registers
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();         // every wave is done with the ring
+      asm volatile("" ::: "memory");
     }
-    wait_vmcnt<0>();
-    for (int i = 1; i < kPrefetch && i < n_t; ++i) issue(i);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    for (int i = 0; i < kPrefetch && i < n_t; ++i) issue(i);
+    {   // publish tile 0 with the copies of tiles 1 .. min(2, n_t - 1) still in flight
+      constexpr int kOne = kDmaPerThread < 63 ? kDmaPerThread : 63;
+      constexpr int kTwo = 2 * kDmaPerThread < 63 ? 2 * kDmaPerThread : 63;
+      static_assert(kPrefetch == 3, "the first wait counts two later tiles");
+      if (n_t >= 3) {
+        wait_vmcnt<kTwo>();
+      } else if (n_t == 2) {
+        wait_vmcnt<kOne>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    if (p.nsplit < 0) s_bad = (int)touched;   // never true: keeps the touching loads
     // One score tile is enough: the softmax turns it into P (pb) before the
     // next tile's scores are computed into the same registers.
     f32x16_t sc;
-    scores_and_values(sc, 0, 0, std::false_type{});
+    scores_and_values(sc, 0, 0, std::false_type{}, -1, std::integral_constant<int, 0>{});
 
-    // Step i: softmax of tile i; publish tile i + 1; copy tile i + kPrefetch
-    // into the stage tile i - 1 left (every wave is past step i - 1 once
-    // the barrier opens); scores of tile i + 1 together with the values of
-    // tile i. The last tile is peeled off (no next tile), so the loop has no
-    // branch that would make the compiler copy O^T between register sets.
+    // Step i: softmax of tile i; publish tile i + 1; scores of tile i + 1
+    // together with the values of tile i, with the copies of tile
+    // i + kPrefetch spread between them (into the stage tile i - 1 left:
+    // every wave is past step i - 1 once the barrier opens). The steps run
+    // in three loops by what they copy (whole contiguous tiles, with one lane
+    // offset per op; partial or paged tiles; nothing), and the last tile is
+    // peeled off (no next tile): a branch between variants inside one loop
+    // makes the compiler move O^T between register sets.
     static_assert(kPrefetch == kStages - 1, "the copy reuses the stage of tile i - 1");
-    for (int i = 0; i + 1 < n_t; ++i) {
+    auto step = [&](int i, auto mode) __attribute__((always_inline)) {
       softmax(sc, i);
       publish(i + 1);
-      if (i + kPrefetch < n_t) issue(i + kPrefetch);
-      scores_and_values(sc, (i + 1) % kStages, i % kStages, std::true_type{});
-    }
+      constexpr int MODE = decltype(mode)::value;
+      if constexpr (MODE != 0) issue_prep(i + kPrefetch);
+      scores_and_values(sc, (i + 1) % kStages, i % kStages, std::true_type{},
+                        MODE != 0 ? i + kPrefetch : -1, mode);
+    };
+    const int n_whole = PAGED ? 0 : (t_end - t_begin) / kTile;   // tiles 0 .. n_whole-1 are whole
+    int i = 0;
+    for (; i + 1 < n_t && i + kPrefetch < n_whole; ++i) step(i, std::integral_constant<int, 1>{});
+    for (; i + 1 < n_t && i + kPrefetch < n_t; ++i) step(i, std::integral_constant<int, 2>{});
+    for (; i + 1 < n_t; ++i) step(i, std::integral_constant<int, 0>{});
     softmax(sc, n_t - 1);
     values((n_t - 1) % kStages);
   }
