@@ -104,7 +104,10 @@ __device__ __forceinline__ int swz(int r) {
 // back in place; plain VALU arithmetic on them makes the compiler move all of
 // them through VGPRs on every loop trip). The s_nops cover the MFMA-write to
 // v_accvgpr_read and v_accvgpr_write to MFMA wait states.
-__device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kDB], float alpha) {
+// Tile t of a wave's O^T covers head block t % HB; alpha[t % HB] is this
+// lane's factor for it.
+template <int HB>
+__device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kDB], const float (&alpha)[HB]) {
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
   for (int db = 0; db < kDB; ++db)
@@ -116,7 +119,7 @@ __device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kDB], float alpha) {
           "v_mul_f32 %1, %1, %2\n\t"
           "v_accvgpr_write_b32 %0, %1"
           : "+a"(x), "=&v"(t)
-          : "v"(alpha));
+          : "v"(alpha[db % HB]));
       acc[db][i] = x;
     }
   asm volatile("s_nop 7" ::: "memory");
@@ -131,7 +134,17 @@ template <int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   static_assert(kDmaTile % NW == 0, "every thread copies the same number of chunks");
   constexpr int kDmaPerThread = kDmaTile / NW;
+  // O^T += V^T P^T is split by value dims: a wave owns the O^T tiles of
+  // kPvHB head blocks x kPvDB dim blocks (all heads of the workgroup x
+  // 512 / NW dims when NW is 2 or 4; its own heads x all dims otherwise), so
+  // each V^T byte is read from LDS by one wave; P^T goes through LDS.
+  constexpr int kPvHB = NW == 3 ? 1 : NW;
+  constexpr int kPvDB = kDB / kPvHB;
   __shared__ __attribute__((aligned(1024))) char s_lat[kStages * kTileB];
+  __shared__ __attribute__((aligned(16))) char s_p[NW * kHW * 64];   // P^T rows, 64 B per head
+  __shared__ float s_alpha[NW * kHW];                               // rescale factors
+  __shared__ float s_l[NW * kHW];                                   // softmax sums at the end
+  __shared__ __attribute__((aligned(16))) int s_flag[4];
   __shared__ int s_bt[PAGED ? kBtWin : 1];
   __shared__ int s_bad;
 
@@ -293,55 +306,94 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   for (int db = 0; db < kDB; ++db) oacc[db] = f32x16_t{};
   float m_ref = -INFINITY, l_run = 0.0f;
   const float c = p.scale_log2;
-  bf16x8_t pb[2];   // P^T of the tile being consumed, [16-token half]
+  bf16x8_t pb[2];   // P of this wave's heads for the latest softmax, [k-step]
 
-  // S^T of the tile in stage `stage` (36 dependent MFMAs), interleaved with
-  // O^T += V^T P^T for the tile in stage `pv_stage` (32 independent ones)
-  // when WITH_PV: the value MFMAs fill the latency between the score MFMAs.
-  // Operand reads run kAhead MFMA pairs ahead through register rings;
-  // the scheduling barriers keep the compiler from hoisting all 68 reads
-  // (which would not fit in registers).
+  // Operand reads run kAhead MFMAs ahead through register rings; the
+  // scheduling barriers keep the compiler from hoisting all of them (which
+  // would not fit in registers).
   auto read_k = [&](const char* sk, int kk) __attribute__((always_inline)) {
     return *(const bf16x8_t*)(sk + k_base[kk % 4] + 4096 * (kk / 4));
   };
-  auto read_v = [&](const char* sv, int idx) __attribute__((always_inline)) {   // idx = 16 * mm + db
-    const int mm = idx / kDB, db = idx % kDB;
+  auto read_v = [&](const char* sv, int mm, int db) __attribute__((always_inline)) {
     const char* vb = sv + 4096 * (db / 2) + 2048 * mm;
     const bf16x4_t lo = ds_read_tr16(vb + v_base[db & 1][0]);
     const bf16x4_t hi = ds_read_tr16(vb + v_base[db & 1][1]);
     return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  // P^T fragment of head block hb, k-step ks: lane (lr, hf) reads the
+  // 16 bytes lane (lr, hf) of the owning wave wrote as its pb[ks]. Rows are
+  // 64 bytes with the chunk XOR-swizzled by (lr / 4) % 4: the 16 lanes of a
+  // read or write then cover 16 distinct 16-byte bank groups.
+  auto p_addr = [&](int ks, int hb) __attribute__((always_inline)) {
+    return s_p + (hb * kHW + lr) * 64 + 16 * ((2 * ks + hf) ^ ((lr >> 2) & 3));
+  };
+  auto read_p = [&](int ks, int hb) __attribute__((always_inline)) {
+    return *(const bf16x8_t*)p_addr(ks, hb);
+  };
+  auto head_block = [&](int hbi) __attribute__((always_inline)) {
+    return kPvHB == 1 ? wave : hbi;
+  };
+  auto dim_block = [&](int dbi) __attribute__((always_inline)) {
+    return kPvHB == 1 ? dbi : kPvDB * wave + dbi;
+  };
+  // The 32 value MFMAs in the order idx = 16 ks + kPvHB dbi + hbi: V^T
+  // group G = idx / kPvHB (k-step G / kPvDB, dim block G % kPvDB) serves
+  // kPvHB MFMAs in a row; the P^T fragments of a k-step stay in registers.
+  // V^T groups are read kAhead MFMAs ahead through a ring; with four head
+  // blocks the P^T fragments of k-step 1 replace those of k-step 0 right
+  // after their last use (three MFMAs ahead), otherwise both k-steps are
+  // read up front.
+  constexpr int kV0 = (kAhead + kPvHB - 1) / kPvHB;   // V^T groups read before the loop
+  constexpr int kVS = kV0 + 1;                        // V^T ring slots
+  constexpr bool kPReload = kPvHB == 4;
+  constexpr int kPS = kPReload ? kPvHB : 2 * kPvHB;   // P^T slots
+  auto v_group = [&](const char* sv, int G) __attribute__((always_inline)) {
+    return read_v(sv, G / kPvDB, dim_block(G % kPvDB));
   };
   // When dma_tile >= 0, the copies of that tile are issued one every
   // kDmaStride MFMA steps: an op that has to wait for room in the memory
   // queues then stalls a wave for part of an MFMA's latency, not all at once.
   constexpr int kDmaStride = kKSteps / kDmaPerThread;
   static_assert(kKSteps % kDmaPerThread == 0, "DMA ops spread evenly over the score steps");
+  // S^T of the tile in stage `stage` (36 dependent MFMAs) interleaved, when
+  // WITH_PV, with the 32 value MFMAs of the tile in `pv_stage`: the value
+  // MFMAs fill the latency between the score MFMAs.
   auto scores_and_values = [&](f32x16_t& s, int stage, int pv_stage, auto with_pv, int dma_tile,
                                auto dma_mode) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
     constexpr int DMA = decltype(dma_mode)::value;   // 0: no copies, else issue_op's MODE
     const char* sk = s_lat + stage * kTileB;
     const char* sv = s_lat + pv_stage * kTileB;
-    bf16x8_t kr[kAhead + 1], vr[kAhead + 1];
+    bf16x8_t kr[kAhead + 1], vr[kVS], pr[kPS];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) kr[j] = read_k(sk, j);
     if constexpr (PV) {
 #pragma unroll
-      for (int j = 0; j < kAhead; ++j) vr[j] = read_v(sv, j);
+      for (int G = 0; G < kV0; ++G) vr[G % kVS] = v_group(sv, G);
+#pragma unroll
+      for (int j = 0; j < kPS; ++j) pr[j] = read_p(j / kPvHB, head_block(j % kPvHB));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
       if (kk + kAhead < kKSteps) kr[(kk + kAhead) % (kAhead + 1)] = read_k(sk, kk + kAhead);
-      if (PV && kk + kAhead < 2 * kDB) vr[(kk + kAhead) % (kAhead + 1)] = read_v(sv, kk + kAhead);
+      if constexpr (PV) {
+        // V^T group first used at idx = kPvHB G is read at kPvHB G - kAhead.
+        if ((kk + kAhead) % kPvHB == 0) {
+          const int G = (kk + kAhead) / kPvHB;
+          if (G >= kV0 && G < 2 * kPvDB) vr[G % kVS] = v_group(sv, G);
+        }
+      }
       if (kk == 0) {
         s = mma_v_first(kr[0], qB[0]);
       } else {
         mma_v(s, kr[kk % (kAhead + 1)], qB[kk]);
       }
       if (PV && kk < 2 * kDB) {
-        const int mm = kk / kDB, db = kk % kDB;
-        oacc[db] = mma(vr[kk % (kAhead + 1)], pb[mm], oacc[db]);
+        const int ks = kk / 16, hbi = kk % kPvHB, t = (kk % 16 / kPvHB) * kPvHB + hbi;
+        const int ps = kPReload ? hbi : ks * kPvHB + hbi;
+        oacc[t] = mma(vr[(kk / kPvHB) % kVS], pr[ps], oacc[t]);
+        if (kPReload && kk >= 16 - kPvHB && kk < 16) pr[hbi] = read_p(1, head_block(hbi));
       }
       if (DMA != 0 && kk % kDmaStride == 0) issue_op(dma_tile, kk / kDmaStride, dma_mode);
       __builtin_amdgcn_sched_barrier(0);
@@ -350,14 +402,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // O^T += V^T P^T alone (the last tile of the range).
   auto values = [&](int pv_stage) __attribute__((always_inline)) {
     const char* sv = s_lat + pv_stage * kTileB;
-    bf16x8_t vr[kAhead + 1];
+    bf16x8_t vr[kVS], pr[kPS];
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) vr[j] = read_v(sv, j);
+    for (int G = 0; G < kV0; ++G) vr[G % kVS] = v_group(sv, G);
+#pragma unroll
+    for (int j = 0; j < kPS; ++j) pr[j] = read_p(j / kPvHB, head_block(j % kPvHB));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int idx = 0; idx < 2 * kDB; ++idx) {
-      if (idx + kAhead < 2 * kDB) vr[(idx + kAhead) % (kAhead + 1)] = read_v(sv, idx + kAhead);
-      oacc[idx % kDB] = mma(vr[idx % (kAhead + 1)], pb[idx / kDB], oacc[idx % kDB]);
+      if ((idx + kAhead) % kPvHB == 0) {
+        const int G = (idx + kAhead) / kPvHB;
+        if (G >= kV0 && G < 2 * kPvDB) vr[G % kVS] = v_group(sv, G);
+      }
+      const int ks = idx / 16, hbi = idx % kPvHB, t = (idx % 16 / kPvHB) * kPvHB + hbi;
+      const int ps = kPReload ? hbi : ks * kPvHB + hbi;
+      oacc[t] = mma(vr[(idx / kPvHB) % kVS], pr[ps], oacc[t]);
+      if (kPReload && idx >= 16 - kPvHB && idx < 16) pr[hbi] = read_p(1, head_block(hbi));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -366,6 +426,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // P in bf16 (pb) and the row sum of the same rounded values. Accumulator
   // register r holds token 32 i + 8*(r/4) + 4*hf + r%4 of the range.
   const uint32_t ones = 0x3f803f80u;
+  bool resc = false;        // this wave's heads need O^T rescaled (wave-uniform)
+  float alpha_own = 1.0f;   // the factor of head lr when resc
   auto softmax = [&](f32x16_t& s, int i) __attribute__((always_inline)) {
     score_wait();
     const int t0 = t_begin + kTile * i;
@@ -382,13 +444,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
                                                      false, false);
     m = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    // Token t0 is live for every head, so m is finite.
+    // Token t0 is live for every head, so m is finite. A rescale of O^T
+    // is recorded here and applied by every wave to its tiles of these
+    // heads once the factors are published (see rescale).
+    resc = false;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64((m - m_ref) * c > kLazy) != 0, 0)) {
       const float m_new = fmaxf(m_ref, m);
-      const float alpha = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+      alpha_own = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
       m_ref = m_new;
-      l_run *= alpha;
-      scale_acc(oacc, alpha);
+      l_run *= alpha_own;
+      resc = true;
     }
     const float mc = m_ref * c;
     float ps = 0.0f;
@@ -404,6 +469,36 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
       ps = dot2_bf16(w.w, ones, ps);
     }
     l_run += ps;
+  };
+
+  // Hand P (and a pending rescale) of this wave's heads to the others:
+  // the barrier first, because every wave reads the buffer during the
+  // previous step's values; the next barrier (publish) makes the writes
+  // visible.
+  auto exchange = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) *(bf16x8_t*)p_addr(mm, wave) = pb[mm];
+    if (resc && hf == 0) s_alpha[wave * kHW + lr] = alpha_own;
+    if (lane == 0) s_flag[wave] = resc ? 1 : 0;
+  };
+  // After the publish barrier: scale this wave's O^T tiles of every head
+  // whose owner recorded a rescale. Before the first values O^T is zero.
+  auto rescale = [&](int i) __attribute__((always_inline)) {
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= s_flag[w];
+    if (__builtin_expect(any != 0, 0) && i > 0) {
+      float a[kPvHB];
+#pragma unroll
+      for (int hbi = 0; hbi < kPvHB; ++hbi) {
+        const int hb = head_block(hbi);
+        a[hbi] = s_flag[hb] ? s_alpha[hb * kHW + lr] : 1.0f;
+      }
+      scale_acc(oacc, a);
+    }
   };
 
   if (n_t > 0) {
@@ -487,7 +582,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     static_assert(kPrefetch == kStages - 1, "the copy reuses the stage of tile i - 1");
     auto step = [&](int i, auto mode) __attribute__((always_inline)) {
       softmax(sc, i);
+      exchange();
       publish(i + 1);
+      rescale(i);
       constexpr int MODE = decltype(mode)::value;
       if constexpr (MODE != 0) issue_prep(i + kPrefetch);
       scores_and_values(sc, (i + 1) % kStages, i % kStages, std::true_type{},
@@ -499,20 +596,26 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     for (; i + 1 < n_t && i + kPrefetch < n_t; ++i) step(i, std::integral_constant<int, 2>{});
     for (; i + 1 < n_t; ++i) step(i, std::integral_constant<int, 0>{});
     softmax(sc, n_t - 1);
+    exchange();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    rescale(n_t - 1);
     values((n_t - 1) % kStages);
   }
 
-  // ---- epilogue: l = both halves' shares. The scaled O^T goes through LDS
-  // (free once every wave is past its last tile) so that every store writes
-  // one head's 1 KB row: row h of the workgroup at byte h * kOutRow (padded:
-  // the 32 heads a wave writes at once spread over the banks).
+  // ---- epilogue: l = both halves' shares, published per head. The scaled
+  // O^T tiles go through LDS (free once every wave is past its last tile)
+  // so that every store writes one head's 1 KB row: row h of the workgroup
+  // at byte h * kOutRow (padded: the 32 heads written at once spread over
+  // the banks).
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
                                                     false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
-  float inv;
+  if (hf == 0) s_l[wave * kHW + lr] = l_tot;
   __bf16* dst;   // the workgroup's first row (head hg * 32 * NW)
   if (p.nsplit == 1) {
-    inv = bad ? __builtin_nanf("") : 1.0f / l_tot;
     dst = (__bf16*)p.o + ((int64_t)b * p.n_heads + hg * kHW * NW) * kR;
   } else {
     // Partial of this split: O / l in bf16 (half the traffic of the fp32
@@ -520,7 +623,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     // m in the log2 domain and l in fp32.
     // A piece with a block outside the pool leaves a NaN sum, which makes
     // the merged row NaN.
-    inv = n_t > 0 ? 1.0f / l_tot : 0.0f;
     const int64_t w = ((int64_t)b * p.nsplit + split) * p.n_heads + head;
     dst = p.ws_o + (((int64_t)b * p.nsplit + split) * p.n_heads + hg * kHW * NW) * kR;
     if (hf == 0) {
@@ -530,19 +632,25 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   }
   constexpr int kOutRow = kR * 2 + 8;
   static_assert(kHW * kMaxWaves * kOutRow <= kStages * kTileB, "output rows fit in the ring");
-  __syncthreads();   // every wave is done with the latent tiles
-  // Accumulator register r of block db holds value 32*db + 8*(r/4) + 4*hf + r%4.
-  char* my_rows = s_lat + (wave * kHW) * kOutRow;
+  __syncthreads();   // every wave is done with the latent tiles; every sum is published
+  // Tile t covers head block head_block(t % kPvHB) and dim block
+  // dim_block(t / kPvHB); register r holds dim 32 db + 8 (r/4) + 4 hf + r%4
+  // of head lr of the block.
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
+  for (int t = 0; t < kDB; ++t) {
+    const int hrow = head_block(t % kPvHB) * kHW + lr, db = dim_block(t / kPvHB);
+    const float l_h = s_l[hrow];
+    const float inv = p.nsplit == 1 ? (bad ? __builtin_nanf("") : 1.0f / l_h)
+                                    : (n_t > 0 ? 1.0f / l_h : 0.0f);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const bf16x4_t v = {(__bf16)(oacc[db][4 * g4 + 0] * inv), (__bf16)(oacc[db][4 * g4 + 1] * inv),
-                          (__bf16)(oacc[db][4 * g4 + 2] * inv), (__bf16)(oacc[db][4 * g4 + 3] * inv)};
-      *(bf16x4_t*)(my_rows + lr * kOutRow + 2 * (32 * db + 8 * g4 + 4 * hf)) = v;
+      const bf16x4_t v = {(__bf16)(oacc[t][4 * g4 + 0] * inv), (__bf16)(oacc[t][4 * g4 + 1] * inv),
+                          (__bf16)(oacc[t][4 * g4 + 2] * inv), (__bf16)(oacc[t][4 * g4 + 3] * inv)};
+      *(bf16x4_t*)(s_lat + hrow * kOutRow + 2 * (32 * db + 8 * g4 + 4 * hf)) = v;
     }
-  // A wave reads back only its own rows: its LDS writes are complete once
-  // lgkmcnt drains, which the compiler waits for before the reads.
+  }
+  __syncthreads();   // every wave's slice of every row is written
+  char* my_rows = s_lat + (wave * kHW) * kOutRow;
   __bf16* my_dst = dst + (int64_t)(wave * kHW) * kR;
 #pragma unroll 4
   for (int r = 0; r < kHW; ++r) {
