@@ -45,6 +45,8 @@ constexpr int kBlockN = 64;    // keys per tile
 constexpr int kBtWin = 256;    // block-table entries cached in LDS
 constexpr int kXcds = 8;       // accelerator complex dies, each with its own L2
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
+constexpr int kSortMax = 128;  // ragged batches with up to this many (sequence, tile) pairs are
+                               // dispatched in work order
 
 template <bool BF16>
 struct Mfma;
@@ -128,11 +130,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     }
   }
   const int per_level = p.batch * p.n_heads;
-  const int level = work / per_level;
+  int level = work / per_level;
   const int rest = work % per_level;
-  const int h = rest % p.n_heads;
-  const int b = rest / p.n_heads;
-  const int kvh = h / p.group;
+  int h = rest % p.n_heads;
+  int b = rest / p.n_heads;
 
   // The sequence's query rows, keys and offset: shared by the batch, or
   // (ragged batch) its own, with its query rows packed after the previous
@@ -141,6 +142,52 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   int64_t q_row0 = (int64_t)b * p.seq_q;   // the sequence's first row of q and o
   int qt;                                    // query tile of this work item
   bool poisoned = false;                     // bad sizes or block ids: NaN rows
+  if constexpr (VARLEN) {
+    // Ragged batches: the (sequence, tile level) pairs go out heaviest first
+    // by their key-tile steps (longest processing time first), so that a
+    // light tile of a short history does not hold a slot while heavier ones
+    // of other sequences wait. Workgroup w takes pair number w / n_heads of
+    // that order, head w % n_heads; the pairs are those of the level order
+    // (level l: the sequence's tile tiles - 1 - l). Every thread ranks one
+    // candidate pair against all others (up to kSortMax pairs; larger
+    // batches keep the level order).
+    const int n_cand = p.batch * p.q_tiles;
+    if (n_cand <= kSortMax) {
+      __shared__ int s_steps[kSortMax];
+      __shared__ int s_sel;
+      const int t = threadIdx.x;
+      int steps = -1;
+      if (t < n_cand) {
+        const int cb = t / p.q_tiles, cl = t % p.q_tiles;
+        const int c0 = p.cu_q[cb], c1 = p.cu_q[cb + 1];
+        const int cq = (c1 - c0 + kBlockM - 1) / kBlockM - 1 - cl;   // its query tile
+        if (c0 >= 0 && c1 >= c0 && c1 <= p.total_q && cq >= 0) {
+          const int rows = min(kBlockM, c1 - c0 - cq * kBlockM);
+          const int64_t last = (int64_t)p.kv_lens[cb] - (c1 - c0) + (int64_t)cq * kBlockM + rows - 1;
+          const int64_t st = last < 0 ? 0 : last / kBlockN + 1;
+          steps = st > (1 << 30) ? (1 << 30) : (int)st;
+        }
+      }
+      if (t < kSortMax) s_steps[t] = steps;
+      if (t == 0) s_sel = -1;
+      __syncthreads();
+      if (steps >= 0) {
+        int rank = 0;
+        for (int u = 0; u < n_cand; ++u) {
+          const int su = s_steps[u];
+          rank += su > steps || (su == steps && u < t);
+        }
+        if (rank == work / p.n_heads) s_sel = t;
+      }
+      __syncthreads();
+      if (s_sel < 0) return;   // uniform: no pair of this rank
+      b = s_sel / p.q_tiles;
+      level = s_sel % p.q_tiles;
+      h = work % p.n_heads;
+    }
+  }
+  const int kvh = h / p.group;
+
   if constexpr (VARLEN) {
     const int s0 = p.cu_q[b], s1 = p.cu_q[b + 1];
     // Rows outside [0, total_q): nothing of this sequence can be written.
