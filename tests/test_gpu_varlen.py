@@ -120,3 +120,18 @@ def test_varlen_bad_sequences_get_nan_rows_only():
     ref = O.prefill_varlen(c.q, c.k, c.v, c.cu_q, c.seq_kv, 4, 2, c.scale, c.block_table, 16,
                            rows=list(range(40, 90)))
     check(o[40:90], ref, "bf16", "the clean sequence")
+
+
+def test_varlen_work_order_is_invisible_in_the_results():
+    # A ragged batch with at most 128 (sequence, query tile) pairs is dispatched
+    # heaviest pair first; a larger one (here forced by a loose max_seq_q bound,
+    # whose extra tiles are empty) keeps the plain order. Each pair is computed
+    # by one workgroup either way, so the two runs agree bit for bit.
+    say("case: ragged prefill, 20 seqs, work-sorted order vs plain order (bitwise) + oracle")
+    c = inputs.varlen_prefill_case(8, batch=20, q_lo=1, q_hi=380, cached_lo=0, cached_hi=600,
+                                   n_heads=4, n_kv_heads=2)
+    o_sorted = run(c)                      # 20 * 3 = 60 pairs
+    o_plain = run(c, max_seq_q=900)        # 20 * 8 = 160 pairs
+    assert torch.equal(o_sorted, o_plain)
+    ref = O.prefill_varlen(c.q, c.k, c.v, c.cu_q, c.seq_kv, 4, 2, c.scale, c.block_table, 16)
+    check(host(o_sorted), ref, "bf16", "all rows of 20 sequences")
