@@ -11,10 +11,13 @@
 // busy with two waves, and one copy of each key tile serves 256 rows. Key
 // tiles of 64 rows reach LDS by global -> LDS copies (no staging
 // registers) into two rings, K one tile ahead of V, so that one step
-// overlaps the MFMAs of the next tile's scores with the VALU softmax of the
-// current one:
-//   step t: copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T while P(t) = exp2(S(t)
-//   - m); O^T += V(t)^T P(t)^T; row max of S(t+1); one barrier.
+// overlaps MFMAs with the VALU softmax:
+//   step t (bf16): copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T; O^T += V(t)^T
+//   P(t)^T while the VALU takes the row max of S(t+1) and makes P(t+1) =
+//   exp2(S(t+1) - m) in bf16 (made again in the rare step that moves m);
+//   one barrier. P, not S, is what crosses the barrier.
+//   step t (fp32): copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T while P(t) =
+//   exp2(S(t) - m); O^T += V(t)^T P(t)^T; row max of S(t+1); one barrier.
 // The LDS image of a tile spreads rows over the banks so that the operand
 // reads are free of bank conflicts with lane-base-plus-immediate addresses:
 //   S^T = K Q^T on 32x32 MFMAs (Q^T in registers as the B operand): in the
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   // wave's share of the copies, 16 bytes per lane. Rows past last_key copy
   // row last_key instead (finite data; the mask and P = 0 discard them), so
   // every wave always issues kCopiesW copies.
-  auto issue = [&](const char* g, int kt, char* slot) {
+  auto issue = [&](const char* g, int kt, char* slot) __attribute__((always_inline)) {
     const int k0 = kt * kBlockN;
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(slot);
 #pragma unroll
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const int kt_open = min(min((wave_pos_first + 1) / kBlockN, seq_kv / kBlockN), n_w);
 
     // S^T = K Q^T for the K tile at sK.
-    auto qk = [&](const char* sK, f32x16_t (&s)[2]) {
+    auto qk = [&](const char* sK, f32x16_t (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16_t acc = f32x16_t{};
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       }
     };
     // Accumulator register r of key block kb holds key k0 + 32*kb + 8*(r/4) + 4*hf + r%4.
-    auto mask = [&](int k0, f32x16_t (&s)[2]) {
+    auto mask = [&](int k0, f32x16_t (&s)[2]) __attribute__((always_inline)) {
       const int lim = min(my_pos, seq_kv - 1) - (k0 + 4 * hf);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // 2^kLazy, and then O and l are rescaled. (maximum, not maxnum: no
     // canonicalising moves; scores carry no NaN unless the inputs do, and
     // then the row is NaN either way.)
-    auto update_max = [&](const f32x16_t (&s)[2]) {
+    auto row_max = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -357,59 +360,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[kb][r]), s[kb][r + 1]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
-      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > kLazy) != 0) {   // wave-uniform
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha =
-            m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      }
+      return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     };
-    // P = 2^((s - m_ref) c), l += row sums of P, O^T += V^T P^T.
-    auto exp_pv = [&](f32x16_t (&s)[2], const char* sV) {
-      // Key 0 is visible to every row, so m_ref is finite from the first tile on.
-      const float mc = m_ref == -INFINITY ? 0.0f : m_ref * c;
+    // True (and O, l rescaled to the new reference max) if the max moved.
+    auto rescale_if_grown = [&](float mx) __attribute__((always_inline)) -> bool {
+      if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > kLazy) == 0) return false;   // wave-uniform
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha =
+          m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      return true;
+    };
+    auto update_max = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) {
+      rescale_if_grown(row_max(s));
+    };
+    // fp32: P = 2^((s - m_ref) c) in place, l += row sums of P, O^T += V^T P^T.
+    auto exp_pv = [&](f32x16_t (&s)[2], const char* sV) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sv = s[kb][r];
-          const float x = BF16 ? fmaf(sv, c, -mc) : (sv - m_ref) * c;
-          s[kb][r] = __builtin_amdgcn_exp2f(x);   // masked: exp2(-inf) = 0
-        }
-      if constexpr (BF16) {
-        float psum = 0.0f;
-        const uint32_t ones = 0x3f803f80u;
-        const int g16 = lane / 16, i16 = lane % 16;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            bf16x8_t pb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[kb][8 * mm + j];
-            const auto w = __builtin_bit_cast(uint4, pb);
-            psum = dot2_bf16(w.x, ones, psum);
-            psum = dot2_bf16(w.y, ones, psum);
-            psum = dot2_bf16(w.z, ones, psum);
-            psum = dot2_bf16(w.w, ones, psum);
-            const int lo_row = kb * 32 + 16 * mm + 4 * hf + i16 / 4;
-            const int hi_row = lo_row + 8;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const int chunk = 4 * db + 2 * (g16 % 2) + (i16 % 4) / 2;
-              const bf16x4_t lo = ds_read_tr16(sV + row_off(lo_row) + chunk * 16 + 8 * (i16 % 2));
-              const bf16x4_t hi = ds_read_tr16(sV + row_off(hi_row) + chunk * 16 + 8 * (i16 % 2));
-              const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              oacc[db] = M::mma(a, pb, oacc[db]);
-            }
-          }
-        }
-        l_run += psum;
-      } else {
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = __builtin_amdgcn_exp2f((s[kb][r] - m_ref) * c);   // masked: exp2(-inf) = 0
+      if constexpr (!BF16) {
         float psum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -431,6 +406,69 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       }
     };
 
+    // bf16: P of the tile whose P V comes next, made as soon as that tile's
+    // scores are known (one step ahead of its P V), so that the scores live
+    // only within a step and the exp2 work runs beside the P V MFMAs.
+    bf16x8_t pc[2][2];   // [key block][16-key half]
+    // P = 2^((s - m_ref) c) into pc; returns this lane's row sum of P.
+    auto make_p = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
+      float psum = 0.0f;
+      if constexpr (BF16) {
+        const float mc = m_ref == -INFINITY ? 0.0f : m_ref * c;
+        const uint32_t ones = 0x3f803f80u;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            bf16x8_t pb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)   // masked: exp2(-inf) = 0
+              pb[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * mm + j], c, -mc));
+            const auto w = __builtin_bit_cast(uint4, pb);
+            psum = dot2_bf16(w.x, ones, psum);
+            psum = dot2_bf16(w.y, ones, psum);
+            psum = dot2_bf16(w.z, ones, psum);
+            psum = dot2_bf16(w.w, ones, psum);
+            pc[kb][mm] = pb;
+          }
+      }
+      return psum;
+    };
+    // O^T += V^T P^T with the P in pc.
+    auto pv = [&](const char* sV) __attribute__((always_inline)) {
+      if constexpr (BF16) {
+        const int g16 = lane / 16, i16 = lane % 16;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const int lo_row = kb * 32 + 16 * mm + 4 * hf + i16 / 4;
+            const int hi_row = lo_row + 8;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int chunk = 4 * db + 2 * (g16 % 2) + (i16 % 4) / 2;
+              const bf16x4_t lo = ds_read_tr16(sV + row_off(lo_row) + chunk * 16 + 8 * (i16 % 2));
+              const bf16x4_t hi = ds_read_tr16(sV + row_off(hi_row) + chunk * 16 + 8 * (i16 % 2));
+              const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              oacc[db] = M::mma(a, pc[kb][mm], oacc[db]);
+            }
+          }
+      }
+    };
+    // bf16 scores of tile t + 1 -> pc, while the P V of tile t (pv, issued
+    // before) runs: P is made with the current reference max, which moves
+    // rarely, and made again if the tile's max moved it.
+    auto next_p = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) {
+      const float mx = row_max(s);
+      float psum = make_p(s);
+      // P stays here, ahead of the rare branch (else the compiler moves it
+      // into both paths, after every MFMA of the step).
+      asm volatile("" : "+v"(psum), "+v"(pc[0][0]), "+v"(pc[0][1]), "+v"(pc[1][0]),
+                   "+v"(pc[1][1]));
+      if (rescale_if_grown(mx)) psum = make_p(s);
+      l_run += psum;
+    };
+
     // ---- prologue: K0, V0 and K1 in LDS; S of tile 0.
     issue(kg, 0, ring(0, 0));
     issue(vg, 0, ring(1, 0));
@@ -445,6 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       qk(ring(0, 0), sc);
       if (kt_open == 0) mask(0, sc);
       update_max(sc);
+      if constexpr (BF16) l_run += make_p(sc);
     }
     __syncthreads();   // K slot 0 is refilled in the first step
 
@@ -463,7 +502,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       }
       const char* sKn = ring(0, (t + 1) & 1);
       const char* sV = ring(1, t & 1);
-      if constexpr (kSteady) {
+      if constexpr (BF16) {
+        if (kSteady || t + 1 < n_w) {
+          f32x16_t sn[2];
+          qk(sKn, sn);
+          pv(sV);
+          if (!kSteady) mask((t + 1) * kBlockN, sn);
+          next_p(sn);
+        } else if (t < n_w) {
+          pv(sV);
+        }
+      } else if constexpr (kSteady) {
         f32x16_t sn[2];
         qk(sKn, sn);
         exp_pv(sc, sV);
