@@ -376,7 +376,12 @@ def test_mla_full_size_sampled_sequences():
     oh = host(o)
     bsel = [0, 7, 13, 31]
     ref = O.mla_decode_latent(c.q_abs, c.latent, c.seq_lens, 512, c.scale, batch_indices=bsel)
-    check(oh[bsel], ref, "bf16", "MLA sequences 0,7,13,31")
+    check(oh[bsel], ref, "bf16", "MLA sequences 0,7,13,31, all heads")
+    # Every sequence (each one is eight context pieces, one workgroup each),
+    # eight heads spread over the four 32-head waves.
+    heads = [0, 17, 33, 50, 64, 95, 100, 127]
+    ref = O.mla_decode_latent(c.q_abs, c.latent, c.seq_lens, 512, c.scale, heads=heads)
+    check(oh[:, heads], ref, "bf16", "MLA all 32 sequences, 8 heads")
 
 
 @pytest.mark.parametrize("lens", [[1000, 37], [1, 64, 65, 129], [4096]])
