@@ -36,14 +36,26 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kHsMax = 32;       // query heads per workgroup
+// Tokens per batch per lane group (K and V rows in flight) and waves per SIMD
+// the kernels of groups of 4 to 7 query heads are built for: the plain
+// kernel streams best with more rows in flight at two waves per SIMD, the
+// kernel with the arms (more VALU per token) with fewer at three (measured).
 #ifndef PKVA_DECODE_UNROLL
-#define PKVA_DECODE_UNROLL 2
+#define PKVA_DECODE_UNROLL 4
 #endif
-constexpr int kUnroll = PKVA_DECODE_UNROLL;  // tokens per batch per lane group (K and V rows in flight)
 #ifndef PKVA_DECODE_WAVES_G4
-#define PKVA_DECODE_WAVES_G4 3
+#define PKVA_DECODE_WAVES_G4 2
 #endif
-constexpr int kWavesG4 = PKVA_DECODE_WAVES_G4;  // waves per SIMD the group-of-4 kernels are built for
+#ifndef PKVA_DECODE_UNROLL_EXT
+#define PKVA_DECODE_UNROLL_EXT 2
+#endif
+#ifndef PKVA_DECODE_WAVES_G4_EXT
+#define PKVA_DECODE_WAVES_G4_EXT 3
+#endif
+constexpr int kUnroll = PKVA_DECODE_UNROLL;
+constexpr int kWavesG4 = PKVA_DECODE_WAVES_G4;
+constexpr int kUnrollExt = PKVA_DECODE_UNROLL_EXT;
+constexpr int kWavesG4Ext = PKVA_DECODE_WAVES_G4_EXT;
 #ifndef PKVA_DECODE_SLOTS_PCT
 #define PKVA_DECODE_SLOTS_PCT 100
 #endif
@@ -147,15 +159,16 @@ __device__ __forceinline__ float arm_logit(const DecodeParams& p, float s, float
 // than the values (K rows D + DX wide, V rows D wide). Scores then live in
 // the exp2 domain (c = 1) instead of raw dot products.
 template <bool BF16, int D, int GMAX, bool PAGED, bool WIDE = false, bool EXT = false, int DX = 0>
-__global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? kWavesG4 : 4)) void decode_partial(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, GMAX >= 8 ? 2 : (GMAX >= 4 ? (EXT ? kWavesG4Ext : kWavesG4) : 4))
+void decode_partial(DecodeParams p) {
   constexpr int E = Lane16<BF16>::E;
   constexpr int LG = D / E;          // lanes per (token, kv head) row
   constexpr int NG = kThreads / LG;  // lane groups per workgroup
   constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int U = GMAX >= 8 ? 2 : kUnroll;  // tokens per batch per lane group
+  constexpr int U = GMAX >= 8 ? 2 : (EXT ? kUnrollExt : kUnroll);  // tokens per batch per lane group
   constexpr int DK = D + DX;         // key width
   constexpr int LX = DX / E;         // lanes that hold a second K chunk
-  static_assert(D % E == 0 && kThreads % LG == 0 && LG <= 16 && kUnroll % 2 == 0,
+  static_assert(D % E == 0 && kThreads % LG == 0 && LG <= 16 && U % 2 == 0,
                 "head size must split into at most 16 lanes of 16 bytes");
   static_assert(DX % E == 0 && LX <= LG && (EXT || DX == 0), "extra key width");
   // Merge buffer: per (sub-row, kv head) slice GMAX*D partial sums + GMAX m and l.
