@@ -138,21 +138,33 @@ __device__ __forceinline__ int span_len(const DecodeParams& p, int b, int* start
   return L;
 }
 
-// tanh(y) = 1 - 2 / (1 + e^(2y)): exp2 and a reciprocal; it saturates to
-// +-1 for large |y| (e^(2y) -> inf or 0) and loses only absolute precision
-// (about 1e-7) near 0.
-__device__ __forceinline__ float tanh_fast(float y) {
-  const float e = __builtin_amdgcn_exp2f(y * (2.0f * kLog2e));
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
+// The logit of a score in the exp2 domain with the layer's arms,
+//   log2(e) (softcap tanh(scale s / softcap) + slope (t - pos))   (softcap > 0)
+//   log2(e) (scale s + slope (t - pos))                            (otherwise),
+// with the constant factors folded: a = scale log2(e) (no softcap) or
+// 2 log2(e) scale / softcap (the exp2 argument of the tanh), cap = softcap
+// log2(e), and alibi = slope log2(e) (t - pos) computed once per token.
+struct ArmConst {
+  float a, cap;
+  bool softcap;
+};
+__device__ __forceinline__ ArmConst arm_const(const DecodeParams& p) {
+  ArmConst k;
+  k.softcap = p.softcap > 0.0f;
+  k.a = k.softcap ? p.scale * p.inv_softcap * (2.0f * kLog2e) : p.scale * kLog2e;
+  k.cap = p.softcap * kLog2e;
+  return k;
 }
-
-// The logit of a score in the exp2 domain with the layer's arms:
-// x = scale * s, then softcap * tanh(x / softcap), plus slope * (t - pos).
-__device__ __forceinline__ float arm_logit(const DecodeParams& p, float s, float slope, int rel) {
-  float x = s * p.scale;
-  if (p.softcap > 0.0f) x = p.softcap * tanh_fast(x * p.inv_softcap);
-  x = fmaf(slope, (float)rel, x);
-  return x * kLog2e;
+__device__ __forceinline__ float arm_logit(const ArmConst& k, float s, float alibi) {
+  if (k.softcap) {
+    const float e = __builtin_amdgcn_exp2f(s * k.a);
+    // tanh(y) = 1 - 2 / (1 + e^(2y)): exp2 and a reciprocal; it saturates to
+    // +-1 for large |y| (e^(2y) -> inf or 0) and loses only absolute
+    // precision (about 1e-7) near 0.
+    const float t = fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+    return fmaf(k.cap, t, alibi);
+  }
+  return fmaf(s, k.a, alibi);
 }
 
 // EXT: the arms (window, softcap, ALiBi, sinks) and keys DX elements wider
@@ -268,10 +280,11 @@ void decode_partial(DecodeParams p) {
           if (li < LX) qx[h] = *(const uint4*)((const char*)p.q + (qoff + D) * ESZ);
         }
         if constexpr (EXT) {
-          if (p.alibi != nullptr) slope[h] = p.alibi[head];
+          if (p.alibi != nullptr) slope[h] = p.alibi[head] * kLog2e;   // exp2 domain
         }
       }
     }
+    const ArmConst ak = arm_const(p);
     float acc[GMAX][E];
     float m[GMAX], l[GMAX];
 #pragma unroll
@@ -354,7 +367,8 @@ void decode_partial(DecodeParams p) {
           for (int h = 0; h < GMAX; ++h) s[u][h] = group_sum<LG>(s[u][h]);
           if constexpr (EXT) {
 #pragma unroll
-            for (int h = 0; h < GMAX; ++h) s[u][h] = arm_logit(p, s[u][h], slope[h], t0 + u * R - qpos);
+            for (int h = 0; h < GMAX; ++h)
+              s[u][h] = arm_logit(ak, s[u][h], slope[h] * (float)(t0 + u * R - qpos));
           }
         }
         load_k(kx, kx2, tn);
