@@ -48,6 +48,7 @@ constexpr int kBlockN = 64;    // keys per tile
 constexpr int kBtWin = 256;    // block-table entries cached in LDS
 constexpr int kXcds = 8;       // accelerator complex dies, each with its own L2
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max moves
+constexpr float kNoMaxSum = 128.0f;   // 2^(kLazy - 1)
 constexpr int kSortMax = 128;  // ragged batches with up to this many (sequence, tile) pairs are
                                // dispatched in work order
 
@@ -458,14 +459,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // bf16 scores of tile t + 1 -> pc, while the P V of tile t (pv, issued
     // before) runs: P is made with the current reference max, which moves
     // rarely, and made again if the tile's max moved it.
+    // The row max is needed only when a P could exceed 2^kLazy: every P is at
+    // most its lane's row sum, so a sum below 2^(kLazy - 1) (a factor of two
+    // covers the bf16 rounding of P and the exp2 error) rules a move of the
+    // reference max out, and the max is then skipped. Where the max is
+    // taken, the decision is the same as always; the results do not change.
     auto next_p = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) {
-      const float mx = row_max(s);
       float psum = make_p(s);
       // P stays here, ahead of the rare branch (else the compiler moves it
       // into both paths, after every MFMA of the step).
       asm volatile("" : "+v"(psum), "+v"(pc[0][0]), "+v"(pc[0][1]), "+v"(pc[1][0]),
                    "+v"(pc[1][1]));
-      if (rescale_if_grown(mx)) psum = make_p(s);
+      if (__builtin_amdgcn_ballot_w64(!(psum < kNoMaxSum && m_ref > -INFINITY)) != 0) {
+        if (rescale_if_grown(row_max(s))) psum = make_p(s);
+      }
       l_run += psum;
     };
 
