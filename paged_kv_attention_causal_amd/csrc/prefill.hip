@@ -262,9 +262,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   // wave's share of the copies, 16 bytes per lane. Rows past last_key copy
   // row last_key instead (finite data; the mask and P = 0 discard them), so
   // every wave always issues kCopiesW copies.
+  // A whole tile (no row past last_key) takes a fixed lane offset per copy.
+  uint32_t whole_off[kCopiesW];
+#pragma unroll
+  for (int jj = 0; jj < kCopiesW; ++jj) {
+    const int x = wave + kWaves * jj;
+    const int row = BF16 ? x + 16 * (lane / 16) : 16 * x + lane / CPR;
+    whole_off[jj] = (uint32_t)row * row_bytes + (lane % CPR) * 16;
+  }
   auto issue = [&](const char* g, int kt, char* slot) __attribute__((always_inline)) {
     const int k0 = kt * kBlockN;
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(slot);
+    if (!PAGED && k0 + kBlockN - 1 <= last_key) {   // uniform
+#pragma unroll
+      for (int jj = 0; jj < kCopiesW; ++jj) {
+        const int x = wave + kWaves * jj;
+        if (kCopies % kWaves != 0 && x >= kCopies) break;
+        dma16(g + (int64_t)(seq_row0 + k0) * row_bytes, whole_off[jj], lds + copy_off(x));
+      }
+      return;
+    }
 #pragma unroll
     for (int jj = 0; jj < kCopiesW; ++jj) {
       const int x = wave + kWaves * jj;
