@@ -26,7 +26,8 @@
 // from the accumulator registers straight to the B operand, and the V^T
 // operand comes from the row-major tile through ds_read_b64_tr_b16. The
 // running max moves only when a head's max grows by more than 2^8 in the
-// exp2 domain (then O and l are rescaled).
+// exp2 domain (then O and l are rescaled), and the tile max is taken only
+// when a row sum of P shows that it could have.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,6 +52,7 @@ constexpr int kDmaTile = kTileB / 1024;   // 1 KB DMA ops per tile (36)
 constexpr int kKSteps = kW / 16;  // 16-deep MFMA steps of the scores (36)
 constexpr int kDB = kR / 32;      // 32-row blocks of O^T (16)
 constexpr float kLazy = 8.0f;
+constexpr float kNoMaxSum = 128.0f;   // 2^(kLazy - 1)
 constexpr int kXcds = 8;          // accelerator complex dies, each with its own L2
 constexpr int kAhead = 4;        // MFMA pairs whose operands are read ahead
 constexpr int kBtWin = 512;       // block ids of a paged latent held in LDS
@@ -437,36 +439,49 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
       for (int r = 0; r < 16; ++r)
         if (8 * (r / 4) + (r % 4) > lim) s[r] = -INFINITY;
     }
-    float m = -INFINITY;
+    // P with the current reference max first; the max is needed only when
+    // a P could exceed 2^kLazy. Every P is at most its lane's row sum, so a
+    // sum below 2^(kLazy - 1) (a factor of two covers the bf16 rounding of P
+    // and the exp2 error) rules a move out and the max is skipped; where it
+    // is taken, the decision is the same as always and so are the results.
+    auto make_p = [&]() __attribute__((always_inline)) -> float {
+      const float mc = m_ref * c;
+      float ps = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2)
-      m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, s[r]), s[r + 1]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
-                                                     false, false);
-    m = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    // Token t0 is live for every head, so m is finite. A rescale of O^T
-    // is recorded here and applied by every wave to its tiles of these
-    // heads once the factors are published (see rescale).
+      for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          pb[mm][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * mm + j], c, -mc));
+        const auto w = __builtin_bit_cast(uint4, pb[mm]);
+        ps = dot2_bf16(w.x, ones, ps);
+        ps = dot2_bf16(w.y, ones, ps);
+        ps = dot2_bf16(w.z, ones, ps);
+        ps = dot2_bf16(w.w, ones, ps);
+      }
+      return ps;
+    };
     resc = false;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64((m - m_ref) * c > kLazy) != 0, 0)) {
-      const float m_new = fmaxf(m_ref, m);
-      alpha_own = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-      m_ref = m_new;
-      l_run *= alpha_own;
-      resc = true;
-    }
-    const float mc = m_ref * c;
-    float ps = 0.0f;
+    float ps = make_p();
+    asm volatile("" : "+v"(ps), "+v"(pb[0]), "+v"(pb[1]));
+    if (__builtin_amdgcn_ballot_w64(!(ps < kNoMaxSum && m_ref > -INFINITY)) != 0) {
+      float m = -INFINITY;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        pb[mm][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * mm + j], c, -mc));
-      const auto w = __builtin_bit_cast(uint4, pb[mm]);
-      ps = dot2_bf16(w.x, ones, ps);
-      ps = dot2_bf16(w.y, ones, ps);
-      ps = dot2_bf16(w.z, ones, ps);
-      ps = dot2_bf16(w.w, ones, ps);
+      for (int r = 0; r < 16; r += 2)
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, s[r]), s[r + 1]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                       false, false);
+      m = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // Token t0 is live for every head, so m is finite. A rescale of O^T
+      // is recorded here and applied by every wave to its tiles of these
+      // heads once the factors are published (see rescale).
+      if (__builtin_amdgcn_ballot_w64((m - m_ref) * c > kLazy) != 0) {
+        const float m_new = fmaxf(m_ref, m);
+        alpha_own = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+        m_ref = m_new;
+        l_run *= alpha_own;
+        resc = true;
+        ps = make_p();
+      }
     }
     l_run += ps;
   };
