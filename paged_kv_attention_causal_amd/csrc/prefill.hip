@@ -13,8 +13,9 @@
 // registers) into two rings, K one tile ahead of V, so that one step
 // overlaps MFMAs with the VALU softmax:
 //   step t (bf16): copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T; O^T += V(t)^T
-//   P(t)^T while the VALU takes the row max of S(t+1) and makes P(t+1) =
-//   exp2(S(t+1) - m) in bf16 (made again in the rare step that moves m);
+//   P(t)^T while the VALU makes P(t+1) = exp2(S(t+1) - m) in bf16 and its
+//   row sums; the row max of S(t+1) is taken only when a row sum shows that
+//   m could move (and P(t+1) is made again in the rare step that moves it);
 //   one barrier. P, not S, is what crosses the barrier.
 //   step t (fp32): copy K(t+2), V(t+1); S(t+1) = K(t+1) Q^T while P(t) =
 //   exp2(S(t) - m); O^T += V(t)^T P(t)^T; row max of S(t+1); one barrier.
