@@ -414,8 +414,9 @@ size_t mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int m
  *           splitting the context). With a split context each piece leaves
  *           its output divided by its own softmax sum in bf16 plus its max
  *           and sum in fp32, and a second kernel merges the pieces.
- *   Built: PKVA_BF16 with kv_lora_rank 512, qk_rope_head_dim 64, n_heads a
- *           multiple of 32 that is at most 128 or a multiple of 128.
+ *   Built: PKVA_BF16 with kv_lora_rank 512, qk_rope_head_dim 64, n_heads
+ *           from 1 to 128 or a multiple of 128. A workgroup always serves 128
+ *           heads, so a smaller head count costs about what 128 heads cost.
  */
 int mla_decode_latent(int dtype, const void* q_abs, const void* latent, void* o_lat,
                       int batch, int n_heads, int kv_lora_rank, int qk_rope_head_dim,

@@ -5,12 +5,14 @@
 // It is multi-query attention with one shared KV head, so a latent tile is
 // staged once per workgroup and serves all of its heads.
 //
-// One workgroup = up to 128 heads of one sequence over a range of its
-// context, one wave per 32 heads. A latent byte read from LDS by a wave feeds
-// its 32 heads (S^T = L Q^T and O^T += V^T P^T on 32x32x16 MFMAs): per wave
-// Q^T stays in VGPRs (144) and O^T for 32 heads x 512 values in the 256
-// AGPRs, so one wave per SIMD. The context of a sequence is split over
-// workgroups to fill the chip; mla_combine merges the pieces.
+// One workgroup = 128 heads of one sequence over a range of its context,
+// one wave per 32 heads (a smaller head count leaves the heads past the last
+// one idle: they compute on a copy of its query and are not stored). A
+// latent byte read from LDS by a wave feeds its 32 heads (S^T = L Q^T on
+// 32x32x16 MFMAs, Q^T in 144 VGPRs); O^T += V^T P^T is split by value dims
+// (each wave owns all 128 heads x 128 of the dims, the 256 AGPRs), so one
+// wave per SIMD. The context of a sequence is split over workgroups to fill
+// the chip; mla_combine merges the pieces.
 //
 // 32-token latent tiles (36 KB) are copied global -> LDS by the DMA path
 // (global_load_lds_dwordx4) three tiles ahead into a four-stage ring. Rows
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // to the 8 XCDs round robin (XCD = id % 8); a run of consecutive items
   // per XCD keeps the pieces of one sequence on one L2, which then reads the
   // sequence's queries from memory once.
-  const int n_hg = p.n_heads / (kHW * NW);
+  const int n_hg = (p.n_heads + kHW * NW - 1) / (kHW * NW);
   int item = blockIdx.x;
   if (gridDim.x % kXcds == 0) item = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
   const int split = item % p.nsplit;
@@ -535,12 +537,20 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     constexpr int kPf = (kPfLines + 64 * NW - 1) / (64 * NW);   // loads per thread
     uint32_t touched = 0;
     {
-      const char* qg = (const char*)p.q + ((int64_t)b * p.n_heads + (hg * NW + wave) * kHW) * kRowB;
+      // Heads past the last one (a head count that leaves part of the
+      // group idle) copy the last head's row: their results are computed
+      // from real data and never stored.
+      const int h0 = (hg * NW + wave) * kHW;   // this wave's first head
+      const char* qb = (const char*)p.q + (int64_t)b * p.n_heads * kRowB;
       const uint32_t qst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(s_lat) +
                            (uint32_t)(wave * kTileB);
 #pragma unroll
       for (int J = 0; J < kDmaTile; ++J)
-        dma16(qg + 8 * (J % 4) * kRowB + 128 * (J / 4), dlane[J % 2], qst + 1024u * J);
+      {
+        const int hq = min(h0 + 8 * (J % 4) + drow, p.n_heads - 1);
+        dma16(qb + 128 * (J / 4), (uint32_t)(hq * kRowB) + (dlane[J % 2] - (uint32_t)(drow * kRowB)),
+              qst + 1024u * J);
+      }
       const int rows = min(t_end - t_begin, kPfTiles * kTile);
 #pragma unroll
       for (int k = 0; k < kPf; ++k) {
@@ -643,7 +653,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     // the merged row NaN.
     const int64_t w = ((int64_t)b * p.nsplit + split) * p.n_heads + head;
     dst = p.ws_o + (((int64_t)b * p.nsplit + split) * p.n_heads + hg * kHW * NW) * kR;
-    if (hf == 0) {
+    if (hf == 0 && head < p.n_heads) {
       store_nt(p.ws_ml + w * 2 + 0, n_t > 0 ? m_ref * c : -INFINITY);
       store_nt(p.ws_ml + w * 2 + 1, n_t > 0 ? l_tot : (bad ? __builtin_nanf("") : 0.0f));
     }
@@ -670,10 +680,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   __syncthreads();   // every wave's slice of every row is written
   char* my_rows = s_lat + (wave * kHW) * kOutRow;
   __bf16* my_dst = dst + (int64_t)(wave * kHW) * kR;
+  const int live_rows = min(kHW, p.n_heads - (hg * NW + wave) * kHW);   // heads that exist
 #pragma unroll 4
   for (int r = 0; r < kHW; ++r) {
-    const u32x4_t v = *(const u32x4_t*)(my_rows + r * kOutRow + 16 * lane);
-    store_nt((u32x4_t*)(my_dst + (int64_t)r * kR + 8 * lane), v);
+    if (r < live_rows) {
+      const u32x4_t v = *(const u32x4_t*)(my_rows + r * kOutRow + 16 * lane);
+      store_nt((u32x4_t*)(my_dst + (int64_t)r * kR + 8 * lane), v);
+    }
   }
 }
 
@@ -689,6 +702,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine(MlaParams p) {
   const int hh = threadIdx.x / (kR / 8);
   const int d = 8 * (threadIdx.x % (kR / 8));
   const int bh = blockIdx.x * kCombineHeads + hh;   // b * n_heads + h
+  if (bh >= p.batch * p.n_heads) return;            // (whole waves)
   const int b = bh / p.n_heads, h = bh % p.n_heads;
   const int L = p.seq_lens[b];
   const bool bad = L < 1 || L > p.max_seq_len;
@@ -732,7 +746,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine(MlaParams p) {
 
 template <int NW>
 int launch_nw(const MlaParams& p, hipStream_t stream) {
-  const int n_items = p.batch * (p.n_heads / (kHW * NW)) * p.nsplit;
+  const int n_items = p.batch * ((p.n_heads + kHW * NW - 1) / (kHW * NW)) * p.nsplit;
   if (p.block_table != nullptr) {
     hipLaunchKernelGGL((mla_kernel<NW, true>), dim3(n_items), dim3(64 * NW), 0, stream, p);
   } else {
@@ -744,7 +758,7 @@ int launch_nw(const MlaParams& p, hipStream_t stream) {
 }  // namespace
 
 bool mla_supported(bool bf16, int kv_lora_rank, int rope_dim, int n_heads) {
-  return bf16 && kv_lora_rank == kR && rope_dim == kP && n_heads % kHW == 0 &&
+  return bf16 && kv_lora_rank == kR && rope_dim == kP && n_heads >= 1 &&
          (n_heads <= kHW * kMaxWaves || n_heads % (kHW * kMaxWaves) == 0);
 }
 
@@ -752,18 +766,15 @@ int mla_heads_per_group(int n_heads) { return min(n_heads, kHW * kMaxWaves); }
 int mla_tile_tokens() { return kTile; }
 
 int launch_mla(const MlaParams& p, hipStream_t stream) {
-  int rc = kEunsupported;
-  switch (mla_heads_per_group(p.n_heads) / kHW) {
-    case 1: rc = launch_nw<1>(p, stream); break;
-    case 2: rc = launch_nw<2>(p, stream); break;
-    case 3: rc = launch_nw<3>(p, stream); break;
-    case 4: rc = launch_nw<4>(p, stream); break;
-    default: break;
-  }
+  // Every head count runs the four-wave workgroup of 128 heads: with fewer
+  // heads the idle ones compute on a copy of the last head's query and are
+  // not stored. (A workgroup of fewer waves would leave SIMDs of its compute
+  // unit idle, as the 144 KB tile ring allows one workgroup per unit.)
+  const int rc = launch_nw<kMaxWaves>(p, stream);
   if (rc != kOk) return rc;
   if (p.nsplit > 1) {
-    static_assert(kHW % kCombineHeads == 0, "head counts are multiples of 32");
-    hipLaunchKernelGGL(mla_combine, dim3(p.batch * p.n_heads / kCombineHeads),
+    const int64_t bh = (int64_t)p.batch * p.n_heads;
+    hipLaunchKernelGGL(mla_combine, dim3((unsigned)((bh + kCombineHeads - 1) / kCombineHeads)),
                        dim3(kCombineThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return kEhip;
   }

@@ -145,7 +145,7 @@ def _mla(L, **kw):
     (dict(dtype=3), EUNSUP),
     (dict(R=256), EUNSUP),
     (dict(Pr=32), EUNSUP),
-    (dict(n_heads=120), EUNSUP),
+    (dict(n_heads=200), EUNSUP),          # above 128 and not a multiple of 128
     (dict(q=NULL), EINVAL),
     (dict(cap=100), EINVAL),
     (dict(maxlen=0), EINVAL),
@@ -167,7 +167,9 @@ def test_mla_workspace_size(L):
     assert L.mla_decode_workspace_size(1, 128, 512, 4096) == 1 * 128 * 128 * per
     # 256 sequences fill the GPU unsplit: no workspace
     assert L.mla_decode_workspace_size(256, 128, 512, 4096) == 0
-    assert L.mla_decode_workspace_size(1, 100, 512, 4096) == 0   # not a multiple of 32
+    # any head count up to 128 (one workgroup of 128 heads, the rest idle)
+    assert L.mla_decode_workspace_size(1, 100, 512, 4096) == 1 * 128 * 100 * per
+    assert L.mla_decode_workspace_size(1, 0, 512, 4096) == 0
     assert L.mla_decode_workspace_size(1, 160, 512, 4096) == 0   # above 128, not a multiple
 
 

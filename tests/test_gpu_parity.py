@@ -399,9 +399,12 @@ def test_mla_split_context(lens):
 
 
 @pytest.mark.parametrize("n_heads,batch,lens", [
-    (32, 3, [200, 31, 97]),        # one wave per workgroup
-    (64, 2, [129, 300]),           # two waves
-    (96, 2, [64, 257]),            # three waves
+    (8, 2, [64, 5]),               # fewer heads than one wave's 32
+    (16, 3, [200, 31, 97]),
+    (32, 3, [200, 31, 97]),        # one wave's heads live, three idle
+    (64, 2, [129, 300]),
+    (96, 2, [64, 257]),
+    (100, 2, [129, 40]),           # a partly live wave
     (256, 2, [150, 33]),           # two workgroups per sequence
     (128, 300, None),              # enough sequences to fill the GPU unsplit (no workspace)
 ])
