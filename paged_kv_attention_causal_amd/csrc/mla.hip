@@ -136,13 +136,14 @@ __device__ __forceinline__ void scale_acc(f32x16_t (&acc)[kDB], const float (&al
 // tile's blocks run past it); every copy then takes its row's address.
 template <int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
+  static_assert(NW == kMaxWaves, "built for four waves of 32 heads");
   static_assert(kDmaTile % NW == 0, "every thread copies the same number of chunks");
   constexpr int kDmaPerThread = kDmaTile / NW;
   // O^T += V^T P^T is split by value dims: a wave owns the O^T tiles of
   // kPvHB head blocks x kPvDB dim blocks (all heads of the workgroup x
-  // 512 / NW dims when NW is 2 or 4; its own heads x all dims otherwise), so
-  // each V^T byte is read from LDS by one wave; P^T goes through LDS.
-  constexpr int kPvHB = NW == 3 ? 1 : NW;
+  // 512 / NW dims), so each V^T byte is read from LDS by one wave; P^T goes
+  // through LDS.
+  constexpr int kPvHB = NW;
   constexpr int kPvDB = kDB / kPvHB;
   __shared__ __attribute__((aligned(1024))) char s_lat[kStages * kTileB];
   __shared__ __attribute__((aligned(16))) char s_p[NW * kHW * 64];   // P^T rows, 64 B per head
@@ -334,23 +335,17 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   auto read_p = [&](int ks, int hb) __attribute__((always_inline)) {
     return *(const bf16x8_t*)p_addr(ks, hb);
   };
-  auto head_block = [&](int hbi) __attribute__((always_inline)) {
-    return kPvHB == 1 ? wave : hbi;
-  };
-  auto dim_block = [&](int dbi) __attribute__((always_inline)) {
-    return kPvHB == 1 ? dbi : kPvDB * wave + dbi;
-  };
+  auto head_block = [&](int hbi) __attribute__((always_inline)) { return hbi; };
+  auto dim_block = [&](int dbi) __attribute__((always_inline)) { return kPvDB * wave + dbi; };
   // The 32 value MFMAs in the order idx = 16 ks + kPvHB dbi + hbi: V^T
   // group G = idx / kPvHB (k-step G / kPvDB, dim block G % kPvDB) serves
   // kPvHB MFMAs in a row; the P^T fragments of a k-step stay in registers.
-  // V^T groups are read kAhead MFMAs ahead through a ring; with four head
-  // blocks the P^T fragments of k-step 1 replace those of k-step 0 right
-  // after their last use (three MFMAs ahead), otherwise both k-steps are
-  // read up front.
+  // V^T groups are read kAhead MFMAs ahead through a ring; the P^T
+  // fragments of k-step 1 replace those of k-step 0 right after their last
+  // use (three MFMAs ahead).
   constexpr int kV0 = (kAhead + kPvHB - 1) / kPvHB;   // V^T groups read before the loop
   constexpr int kVS = kV0 + 1;                        // V^T ring slots
-  constexpr bool kPReload = kPvHB == 4;
-  constexpr int kPS = kPReload ? kPvHB : 2 * kPvHB;   // P^T slots
+  constexpr int kPS = kPvHB;                          // P^T slots
   auto v_group = [&](const char* sv, int G) __attribute__((always_inline)) {
     return read_v(sv, G / kPvDB, dim_block(G % kPvDB));
   };
@@ -394,10 +389,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
         mma_v(s, kr[kk % (kAhead + 1)], qB[kk]);
       }
       if (PV && kk < 2 * kDB) {
-        const int ks = kk / 16, hbi = kk % kPvHB, t = (kk % 16 / kPvHB) * kPvHB + hbi;
-        const int ps = kPReload ? hbi : ks * kPvHB + hbi;
-        oacc[t] = mma(vr[(kk / kPvHB) % kVS], pr[ps], oacc[t]);
-        if (kPReload && kk >= 16 - kPvHB && kk < 16) pr[hbi] = read_p(1, head_block(hbi));
+        const int hbi = kk % kPvHB, t = (kk % 16 / kPvHB) * kPvHB + hbi;
+        oacc[t] = mma(vr[(kk / kPvHB) % kVS], pr[hbi], oacc[t]);
+        if (kk >= 16 - kPvHB && kk < 16) pr[hbi] = read_p(1, head_block(hbi));
       }
       if (DMA != 0 && kk % kDmaStride == 0) issue_op(dma_tile, kk / kDmaStride, dma_mode);
       __builtin_amdgcn_sched_barrier(0);
@@ -418,10 +412,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
         const int G = (idx + kAhead) / kPvHB;
         if (G >= kV0 && G < 2 * kPvDB) vr[G % kVS] = v_group(sv, G);
       }
-      const int ks = idx / 16, hbi = idx % kPvHB, t = (idx % 16 / kPvHB) * kPvHB + hbi;
-      const int ps = kPReload ? hbi : ks * kPvHB + hbi;
-      oacc[t] = mma(vr[(idx / kPvHB) % kVS], pr[ps], oacc[t]);
-      if (kPReload && idx >= 16 - kPvHB && idx < 16) pr[hbi] = read_p(1, head_block(hbi));
+      const int hbi = idx % kPvHB, t = (idx % 16 / kPvHB) * kPvHB + hbi;
+      oacc[t] = mma(vr[(idx / kPvHB) % kVS], pr[hbi], oacc[t]);
+      if (idx >= 16 - kPvHB && idx < 16) pr[hbi] = read_p(1, head_block(hbi));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
