@@ -58,7 +58,8 @@ def to_pool(lat, lens, bs, rng, fill=np.nan):
 
 
 @pytest.mark.parametrize("bs,lens,H", [(16, [4096] * 32, 128), (1, [1000, 37, 600], 128),
-                                       (64, [1, 64, 65, 129, 2000], 32), (8, [300, 5000], 256)])
+                                       (64, [1, 64, 65, 129, 2000], 32), (8, [300, 5000], 256),
+                                       (16, [700, 33, 1500], 16)])
 def test_mla_paged_latent_matches_contiguous_and_oracle(bs, lens, H):
     say(f"case: MLA paged latent bs={bs} lens={lens[:6]}{'...' if len(lens) > 6 else ''} H={H}")
     cap = max(lens)
