@@ -20,11 +20,13 @@
 // inside each group of 8: a DMA op fills 1 KB of the tile with any
 // lane-to-chunk map, and both operand reads stay free of bank conflicts.
 //
-// Per step a wave takes the softmax of tile i (S^T computed in the previous
-// step), then runs the 36 MFMAs of S^T for tile i + 1 interleaved with the
-// 32 of O^T += V^T P^T for tile i. In the accumulator layout lane l owns head
-// l % 32 and 16 of the tile's tokens (the other 16 in lane l ^ 32): the max
-// needs one v_permlane32_swap, the sum stays per lane until the end; P goes
+// Per step a wave hands P of tile i to the others, then runs the 36 MFMAs of
+// S^T for tile i + 1 interleaved with the first 24 of the 32 of
+// O^T += V^T P^T for tile i, and the last 8 with the softmax of tile i + 1
+// between them (so that its VALU work runs beside MFMAs). In the
+// accumulator layout lane l owns head l % 32 and 16 of the tile's tokens
+// (the other 16 in lane l ^ 32): the max needs one v_permlane32_swap, the
+// sum stays per lane until the end; P goes
 // from the accumulator registers straight to the B operand, and the V^T
 // operand comes from the row-major tile through ds_read_b64_tr_b16. The
 // running max moves only when a head's max grows by more than 2^8 in the
@@ -354,46 +356,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // queues then stalls a wave for part of an MFMA's latency, not all at once.
   constexpr int kDmaStride = kKSteps / kDmaPerThread;
   static_assert(kKSteps % kDmaPerThread == 0, "DMA ops spread evenly over the score steps");
-  // S^T of the tile in stage `stage` (36 dependent MFMAs) interleaved, when
-  // WITH_PV, with the 32 value MFMAs of the tile in `pv_stage`: the value
-  // MFMAs fill the latency between the score MFMAs.
-  auto scores_and_values = [&](f32x16_t& s, int stage, int pv_stage, auto with_pv, int dma_tile,
-                               auto dma_mode) __attribute__((always_inline)) {
-    constexpr bool PV = decltype(with_pv)::value;
-    constexpr int DMA = decltype(dma_mode)::value;   // 0: no copies, else issue_op's MODE
+  // S^T of the tile in stage `stage` alone (36 dependent MFMAs): the first
+  // tile of a range.
+  auto scores = [&](f32x16_t& s, int stage) __attribute__((always_inline)) {
     const char* sk = s_lat + stage * kTileB;
-    const char* sv = s_lat + pv_stage * kTileB;
-    bf16x8_t kr[kAhead + 1], vr[kVS], pr[kPS];
+    bf16x8_t kr[kAhead + 1];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) kr[j] = read_k(sk, j);
-    if constexpr (PV) {
-#pragma unroll
-      for (int G = 0; G < kV0; ++G) vr[G % kVS] = v_group(sv, G);
-#pragma unroll
-      for (int j = 0; j < kPS; ++j) pr[j] = read_p(j / kPvHB, head_block(j % kPvHB));
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
       if (kk + kAhead < kKSteps) kr[(kk + kAhead) % (kAhead + 1)] = read_k(sk, kk + kAhead);
-      if constexpr (PV) {
-        // V^T group first used at idx = kPvHB G is read at kPvHB G - kAhead.
-        if ((kk + kAhead) % kPvHB == 0) {
-          const int G = (kk + kAhead) / kPvHB;
-          if (G >= kV0 && G < 2 * kPvDB) vr[G % kVS] = v_group(sv, G);
-        }
-      }
       if (kk == 0) {
         s = mma_v_first(kr[0], qB[0]);
       } else {
         mma_v(s, kr[kk % (kAhead + 1)], qB[kk]);
       }
-      if (PV && kk < 2 * kDB) {
-        const int hbi = kk % kPvHB, t = (kk % 16 / kPvHB) * kPvHB + hbi;
-        oacc[t] = mma(vr[(kk / kPvHB) % kVS], pr[hbi], oacc[t]);
-        if (kk >= 16 - kPvHB && kk < 16) pr[hbi] = read_p(1, head_block(hbi));
-      }
-      if (DMA != 0 && kk % kDmaStride == 0) issue_op(dma_tile, kk / kDmaStride, dma_mode);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -425,7 +403,17 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   const uint32_t ones = 0x3f803f80u;
   bool resc = false;        // this wave's heads need O^T rescaled (wave-uniform)
   float alpha_own = 1.0f;   // the factor of head lr when resc
-  auto softmax = [&](f32x16_t& s, int i) __attribute__((always_inline)) {
+  // The softmax of a tile in three parts, so that the pairs can run between
+  // the value MFMAs of the step that computed the tile's scores:
+  // sm_begin masks tokens past t_end; sm_pair(k) makes P of the lane's
+  // scores 2k and 2k + 1 with the current reference max (bf16, into pb) and
+  // adds them to the row sum; sm_end takes the max only when a P could
+  // exceed 2^kLazy (every P is at most its lane's row sum, so a sum below
+  // 2^(kLazy - 1) rules a move out; a factor of two covers the bf16
+  // rounding of P and the exp2 error), moves the reference max when it grew
+  // by more than that, and then makes P again.
+  float sm_mc = 0.0f, sm_ps = 0.0f;
+  auto sm_begin = [&](f32x16_t& s, int i) __attribute__((always_inline)) {
     score_wait();
     const int t0 = t_begin + kTile * i;
     if (t0 + kTile > t_end) {
@@ -434,29 +422,20 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
       for (int r = 0; r < 16; ++r)
         if (8 * (r / 4) + (r % 4) > lim) s[r] = -INFINITY;
     }
-    // P with the current reference max first; the max is needed only when
-    // a P could exceed 2^kLazy. Every P is at most its lane's row sum, so a
-    // sum below 2^(kLazy - 1) (a factor of two covers the bf16 rounding of P
-    // and the exp2 error) rules a move out and the max is skipped; where it
-    // is taken, the decision is the same as always and so are the results.
-    auto make_p = [&]() __attribute__((always_inline)) -> float {
-      const float mc = m_ref * c;
-      float ps = 0.0f;
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pb[mm][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * mm + j], c, -mc));
-        const auto w = __builtin_bit_cast(uint4, pb[mm]);
-        ps = dot2_bf16(w.x, ones, ps);
-        ps = dot2_bf16(w.y, ones, ps);
-        ps = dot2_bf16(w.z, ones, ps);
-        ps = dot2_bf16(w.w, ones, ps);
-      }
-      return ps;
-    };
+    sm_mc = m_ref * c;
+    sm_ps = 0.0f;
     resc = false;
-    float ps = make_p();
+  };
+  auto sm_pair = [&](const f32x16_t& s, int k) __attribute__((always_inline)) {
+    const int mm = k / 4, j = 2 * (k % 4);
+    const bf16x2_t two = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * mm + j], c, -sm_mc)),
+                          (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * mm + j + 1], c, -sm_mc))};
+    pb[mm][j] = two[0];
+    pb[mm][j + 1] = two[1];
+    sm_ps = dot2_bf16(__builtin_bit_cast(uint32_t, two), ones, sm_ps);
+  };
+  auto sm_end = [&](f32x16_t& s) __attribute__((always_inline)) {
+    float ps = sm_ps;
     asm volatile("" : "+v"(ps), "+v"(pb[0]), "+v"(pb[1]));
     if (__builtin_amdgcn_ballot_w64(!(ps < kNoMaxSum && m_ref > -INFINITY)) != 0) {
       float m = -INFINITY;
@@ -475,12 +454,75 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
         m_ref = m_new;
         l_run *= alpha_own;
         resc = true;
-        ps = make_p();
+        sm_mc = m_ref * c;
+        sm_ps = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sm_pair(s, k);
+        ps = sm_ps;
       }
     }
     l_run += ps;
   };
+  auto softmax = [&](f32x16_t& s, int i) __attribute__((always_inline)) {
+    sm_begin(s, i);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sm_pair(s, k);
+    sm_end(s);
+  };
 
+  // One value MFMA (index idx of 32) with its V^T read-ahead and P^T reload.
+  auto value_step = [&](const char* sv, bf16x8_t (&vr)[kVS], bf16x8_t (&pr)[kPS], int idx)
+      __attribute__((always_inline)) {
+    if ((idx + kAhead) % kPvHB == 0) {
+      const int G = (idx + kAhead) / kPvHB;
+      if (G >= kV0 && G < 2 * kPvDB) vr[G % kVS] = v_group(sv, G);
+    }
+    const int hbi = idx % kPvHB, t = (idx % 16 / kPvHB) * kPvHB + hbi;
+    oacc[t] = mma(vr[(idx / kPvHB) % kVS], pr[hbi], oacc[t]);
+    if (idx >= 16 - kPvHB && idx < 16) pr[hbi] = read_p(1, head_block(hbi));
+  };
+  // A steady step's MFMAs: the 36 score MFMAs of the next tile with the
+  // first 32 - kTail value MFMAs of this one between them, then the last
+  // kTail value MFMAs with the next tile's softmax between them (its VALU
+  // work then runs beside MFMAs instead of after them).
+  constexpr int kTail = 8;   // one softmax pair per value MFMA (16 measured slightly slower)
+  static_assert(kTail % 8 == 0 && kTail <= 2 * kDB, "softmax pairs spread evenly");
+  auto section = [&](f32x16_t& s, int stage, int pv_stage, int dma_tile, auto dma_mode,
+                     int sm_tile) __attribute__((always_inline)) {
+    constexpr int DMA = decltype(dma_mode)::value;   // 0: no copies, else issue_op's MODE
+    const char* sk = s_lat + stage * kTileB;
+    const char* sv = s_lat + pv_stage * kTileB;
+    bf16x8_t kr[kAhead + 1], vr[kVS], pr[kPS];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) kr[j] = read_k(sk, j);
+#pragma unroll
+    for (int G = 0; G < kV0; ++G) vr[G % kVS] = v_group(sv, G);
+#pragma unroll
+    for (int j = 0; j < kPS; ++j) pr[j] = read_p(j / kPvHB, head_block(j % kPvHB));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      if (kk + kAhead < kKSteps) kr[(kk + kAhead) % (kAhead + 1)] = read_k(sk, kk + kAhead);
+      if (kk == 0) {
+        s = mma_v_first(kr[0], qB[0]);
+      } else {
+        mma_v(s, kr[kk % (kAhead + 1)], qB[kk]);
+      }
+      if (kk < 2 * kDB - kTail) value_step(sv, vr, pr, kk);
+      if (DMA != 0 && kk % kDmaStride == 0) issue_op(dma_tile, kk / kDmaStride, dma_mode);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sm_begin(s, sm_tile);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int idx = 2 * kDB - kTail; idx < 2 * kDB; ++idx) {
+      value_step(sv, vr, pr, idx);
+      constexpr int kEvery = kTail / 8;
+      if ((idx - (2 * kDB - kTail)) % kEvery == kEvery - 1) sm_pair(s, (idx - (2 * kDB - kTail)) / kEvery);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sm_end(s);
+  };
   // Hand P (and a pending rescale) of this wave's heads to the others:
   // the barrier first, because every wave reads the buffer during the
   // previous step's values; the next barrier (publish) makes the writes
@@ -588,12 +630,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     }
     if (p.nsplit < 0) s_bad = (int)touched;   // never true: keeps the touching loads
     // One score tile is enough: the softmax turns it into P (pb) before the
-    // next tile's scores are computed into the same registers.
+    // next tile's scores are computed into the same registers (in a step,
+    // the next tile's softmax follows its score MFMAs).
     f32x16_t sc;
-    scores_and_values(sc, 0, 0, std::false_type{}, -1, std::integral_constant<int, 0>{});
+    scores(sc, 0);
+    softmax(sc, 0);
 
-    // Step i: softmax of tile i; publish tile i + 1; scores of tile i + 1
-    // together with the values of tile i, with the copies of tile
+    // Step i: P of tile i to the others; publish tile i + 1; scores of tile
+    // i + 1 together with the values of tile i and then the softmax of tile
+    // i + 1, with the copies of tile
     // i + kPrefetch spread between them (into the stage tile i - 1 left:
     // every wave is past step i - 1 once the barrier opens). The steps run
     // in three loops by what they copy (whole contiguous tiles, with one lane
@@ -602,21 +647,18 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     // makes the compiler move O^T between register sets.
     static_assert(kPrefetch == kStages - 1, "the copy reuses the stage of tile i - 1");
     auto step = [&](int i, auto mode) __attribute__((always_inline)) {
-      softmax(sc, i);
       exchange();
       publish(i + 1);
       rescale(i);
       constexpr int MODE = decltype(mode)::value;
       if constexpr (MODE != 0) issue_prep(i + kPrefetch);
-      scores_and_values(sc, (i + 1) % kStages, i % kStages, std::true_type{},
-                        MODE != 0 ? i + kPrefetch : -1, mode);
+      section(sc, (i + 1) % kStages, i % kStages, MODE != 0 ? i + kPrefetch : -1, mode, i + 1);
     };
     const int n_whole = PAGED ? 0 : (t_end - t_begin) / kTile;   // tiles 0 .. n_whole-1 are whole
     int i = 0;
     for (; i + 1 < n_t && i + kPrefetch < n_whole; ++i) step(i, std::integral_constant<int, 1>{});
     for (; i + 1 < n_t && i + kPrefetch < n_t; ++i) step(i, std::integral_constant<int, 2>{});
     for (; i + 1 < n_t; ++i) step(i, std::integral_constant<int, 0>{});
-    softmax(sc, n_t - 1);
     exchange();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("" ::: "memory");
