@@ -487,6 +487,28 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   // work then runs beside MFMAs instead of after them).
   constexpr int kTail = 8;   // one softmax pair per value MFMA (16 measured slightly slower)
   static_assert(kTail % 8 == 0 && kTail <= 2 * kDB, "softmax pairs spread evenly");
+  // After the publish barrier: scale this wave's O^T tiles of every head
+  // whose owner recorded a rescale. Before the first values O^T is zero.
+  auto rescale_with = [&](const int4 fl, int i) __attribute__((always_inline)) {
+    const int any = fl.x | fl.y | fl.z | fl.w;
+    if (__builtin_expect(any != 0, 0) && i > 0) {
+      float a[kPvHB];
+#pragma unroll
+      for (int hbi = 0; hbi < kPvHB; ++hbi) {
+        const int hb = head_block(hbi);
+        a[hbi] = s_flag[hb] ? s_alpha[hb * kHW + lr] : 1.0f;
+      }
+      scale_acc(oacc, a);
+    }
+  };
+  auto rescale = [&](int i) __attribute__((always_inline)) {
+    rescale_with(*(const int4*)s_flag, i);
+  };
+
+  // The value MFMAs start after kShift score MFMAs, so that the rescale
+  // flags (read from LDS at the section's start) have arrived when a
+  // pending rescale must be applied, before the first of them.
+  constexpr int kShift = 4;
   auto section = [&](f32x16_t& s, int stage, int pv_stage, int dma_tile, auto dma_mode,
                      int sm_tile) __attribute__((always_inline)) {
     constexpr int DMA = decltype(dma_mode)::value;   // 0: no copies, else issue_op's MODE
@@ -499,6 +521,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     for (int G = 0; G < kV0; ++G) vr[G % kVS] = v_group(sv, G);
 #pragma unroll
     for (int j = 0; j < kPS; ++j) pr[j] = read_p(j / kPvHB, head_block(j % kPvHB));
+    const int4 fl = *(const int4*)s_flag;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
@@ -508,7 +531,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
       } else {
         mma_v(s, kr[kk % (kAhead + 1)], qB[kk]);
       }
-      if (kk < 2 * kDB - kTail) value_step(sv, vr, pr, kk);
+      if (kk == kShift) {
+        // The tile's rescale (if any): its flags were read while the first
+        // score MFMAs issued.
+        rescale_with(fl, sm_tile - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kk >= kShift && kk < 2 * kDB - kTail + kShift) value_step(sv, vr, pr, kk - kShift);
       if (DMA != 0 && kk % kDmaStride == 0) issue_op(dma_tile, kk / kDmaStride, dma_mode);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -536,23 +565,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     if (resc && hf == 0) s_alpha[wave * kHW + lr] = alpha_own;
     if (lane == 0) s_flag[wave] = resc ? 1 : 0;
   };
-  // After the publish barrier: scale this wave's O^T tiles of every head
-  // whose owner recorded a rescale. Before the first values O^T is zero.
-  auto rescale = [&](int i) __attribute__((always_inline)) {
-    int any = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) any |= s_flag[w];
-    if (__builtin_expect(any != 0, 0) && i > 0) {
-      float a[kPvHB];
-#pragma unroll
-      for (int hbi = 0; hbi < kPvHB; ++hbi) {
-        const int hb = head_block(hbi);
-        a[hbi] = s_flag[hb] ? s_alpha[hb * kHW + lr] : 1.0f;
-      }
-      scale_acc(oacc, a);
-    }
-  };
-
   if (n_t > 0) {
     // Prologue. Q^T first: each wave copies its 32 heads' rows (36 KB,
     // contiguous in q_abs) into its own stage of the ring with 1 KB DMA ops
@@ -649,7 +661,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     auto step = [&](int i, auto mode) __attribute__((always_inline)) {
       exchange();
       publish(i + 1);
-      rescale(i);
       constexpr int MODE = decltype(mode)::value;
       if constexpr (MODE != 0) issue_prep(i + kPrefetch);
       section(sc, (i + 1) % kStages, i % kStages, MODE != 0 ? i + kPrefetch : -1, mode, i + 1);
