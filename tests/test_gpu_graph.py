@@ -4,7 +4,10 @@ Every entry point takes caller buffers and makes no allocation, memset or
 host query after its first call on a device, so a serving loop can capture
 it. Each case: one eager call to warm up, capture, then three replays with
 the inputs changed in place between them (plus unrelated eager work), each
-replay compared bitwise with an eager call on the same inputs.
+replay compared bitwise with an eager call on the same inputs. Covered:
+paged decode (workspace and static scratch), the push followed by paged
+decode, causal, chunked and ragged prefill, the MLA latent decode and its
+two projections.
 """
 import numpy as np
 import pytest
@@ -113,3 +116,59 @@ def test_graph_mla_latent_decode():
                              attention_scale=c.scale, out=out, workspace=ws)
 
     replay_and_compare(call, out, lambda r: q.copy_(q2[r]))
+
+
+def test_graph_push_then_paged_decode():
+    say("case: push of one K/V row per sequence, then paged decode, in one graph")
+    c = inputs.append_case(0, held_hi=2047)
+    kp, vp = dev(c.k_cache), dev(c.v_cache)
+    bt, pos = i32(c.block_table), i32(c.held)
+    kn, vn = dev(c.k_new), dev(c.v_new)
+    lens = i32(c.held + 1)
+    q = dev(inputs.paged_decode_case(5, batch=64, len_lo=1, len_hi=2, n_heads=32, n_kv_heads=8).q)
+    maxlen = int(c.block_table.shape[1] * 16)
+    ws = torch.empty(pk.attn_decode_workspace_size(64, 32, 8, 128, maxlen), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty_like(q)
+    rng = np.random.default_rng(80)
+    new_rows = [(dev(rng.standard_normal(c.k_new.shape)), dev(rng.standard_normal(c.v_new.shape)))
+                for _ in range(3)]
+
+    def call():
+        pk.kv_append(kn, vn, kp, vp, pos, block_table=bt)
+        pk.attn_decode_paged(q, kp, vp, bt, lens, max_seq_len=maxlen, attention_scale=1 / np.sqrt(128),
+                             out=out, workspace=ws)
+
+    def mutate(r):
+        kn.copy_(new_rows[r][0])
+        vn.copy_(new_rows[r][1])
+
+    # The eager call after each replay writes the same rows again, so both read the same pool.
+    replay_and_compare(call, out, mutate)
+
+
+def test_graph_ragged_prefill_and_mla_projections():
+    say("case: ragged paged prefill, and the MLA absorb and up-projection GEMMs, in graphs")
+    r = inputs.varlen_prefill_case(6, batch=5, q_hi=300, cached_hi=700)
+    rq, rk, rv, rbt = dev(r.q), dev(r.k), dev(r.v), i32(r.block_table)
+    rcu, rkv = i32(r.cu_q), i32(r.seq_kv)
+    rout = torch.empty_like(rq)
+    q2 = [dev(np.random.default_rng(90 + i).standard_normal(r.q.shape)) for i in range(3)]
+
+    def call():
+        pk.attn_prefill_varlen(rq, rk, rv, rcu, rkv, max_seq_q=int(r.q_lens.max()),
+                               attention_scale=r.scale, block_table=rbt, out=rout)
+
+    replay_and_compare(call, rout, lambda i: rq.copy_(q2[i]))
+    w = inputs.mla_proj_case(5, batch=8, n_heads=32)
+    wq, wkb, wvb = dev(w.q), dev(w.k_b), dev(w.v_b)
+    qa = torch.empty((8, 32, 576), dtype=torch.bfloat16, device=DEV)
+    up = torch.empty((8, 32, wvb.shape[1]), dtype=torch.bfloat16, device=DEV)
+    ol = dev(w.o_lat)
+    q3 = [dev(np.random.default_rng(95 + i).standard_normal(w.q.shape)) for i in range(3)]
+
+    def call_proj():
+        pk.mla_absorb_q(wq, wkb, out=qa)
+        pk.mla_up_proj(ol, wvb, out=up)
+
+    replay_and_compare(call_proj, qa, lambda i: wq.copy_(q3[i]))
